@@ -1,0 +1,294 @@
+"""Plain float64 definitions of the attention block (test infrastructure only).
+
+Conventions where the pages leave a step open (each one is listed with its
+reason in the design notes of this repository):
+
+* rotary pairs are adjacent dims (2i, 2i+1); "the first p of the pairs" is then
+  the first p*d dims;
+* pair i rotates by the angle pos * theta**(-2i/d) (the ladder of the full head
+  dim, truncated to the first p*d/2 pairs: the low frequencies are the ones
+  dropped), counter-clockwise;
+* pairs past the rotated fraction are left exactly as they are (angle 0);
+* positions are 0-based; QKNorm is x / sqrt(mean(x^2) + eps) * gain;
+* query head h reads KV head h // G (contiguous groups);
+* a window of W keeps keys j with i - W < j <= i (W keys including the query);
+* global (K=V) layers use the normalised, unrotated key as the value; local
+  layers use the raw v;
+* caches: global layers keep one tensor holding the normalised, unrotated key of
+  every position (slot = position); local layers keep a ring of W slots
+  (slot = position mod W) holding the normalised and rotated key and the raw v.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+import math
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class OracleLayer:
+    """Shape and constants of one attention layer, oracle side."""
+
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    window: int            # 0 = full causal (global layer); W > 0 = sliding window
+    kv_shared: bool        # True = keys reused as values (global layers)
+    rope_theta: float
+    rope_fraction: float   # p: 1.0 on local layers, 0.25 on global layers
+    norm_eps: float = 1e-6
+    softmax_scale: float | None = None   # None = 1/sqrt(head_dim)
+
+    @property
+    def group(self) -> int:
+        if self.n_q_heads % self.n_kv_heads:
+            raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def scale(self) -> float:
+        if self.softmax_scale is None:
+            return 1.0 / math.sqrt(self.head_dim)
+        return float(self.softmax_scale)
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --- QKNorm ------------------------------------------------------------------
+# "Gemma 4 Technical Report" notes, §2 Model Architecture: QKNorm alongside
+# pre- and post-norm RMSNorm.  RMSNorm of one head vector, then the gain.
+
+def qk_norm(x, gain, eps: float) -> np.ndarray:
+    """RMS-normalise the last axis of ``x`` and multiply by ``gain`` (length d)."""
+    x = _f64(x)
+    mean_sq = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(mean_sq + eps) * _f64(gain)
+
+
+# --- RoPE and p-RoPE ---------------------------------------------------------
+# "Gemma 4多模态大模型架构详解", section "p-RoPE（低频剪枝旋转位置编码）": the
+# vector is cut into pairs, each pair is a 2-D vector rotated by an angle that
+# shrinks from the first pair to the last; with p = 0.25 only the first quarter
+# of the pairs carry position and the rest are left alone.  Base 1M on global
+# layers, 10k on local layers ("Gemma 4 Technical Report" notes, §2).
+
+def rotated_pairs(head_dim: int, fraction: float) -> int:
+    """Number of rotated pairs, p * d / 2; it must be a whole number."""
+    n = fraction * head_dim / 2.0
+    if n < 0 or abs(n - round(n)) > 1e-9 or head_dim % 2:
+        raise ValueError(f"p*d/2 = {n} is not a whole number of pairs")
+    return int(round(n))
+
+
+def rope_frequencies(head_dim: int, theta: float, fraction: float) -> np.ndarray:
+    """Angular frequency of each rotated pair i: theta ** (-2 i / d)."""
+    i = np.arange(rotated_pairs(head_dim, fraction), dtype=np.float64)
+    return float(theta) ** (-2.0 * i / head_dim)
+
+
+def rotate(x, positions, theta: float, fraction: float) -> np.ndarray:
+    """Rotate pairs (2i, 2i+1), i < p*d/2, of ``x[..., d]`` by positions * omega_i.
+
+    ``positions`` broadcasts against ``x.shape[:-1]``.  Dims from 2*(p*d/2) on
+    are copied unchanged.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    omega = rope_frequencies(d, theta, fraction)
+    n = omega.size
+    angle = _f64(positions)[..., None] * omega          # [..., n]
+    c, s = np.cos(angle), np.sin(angle)
+    y = x.copy()
+    even = x[..., 0:2 * n:2]
+    odd = x[..., 1:2 * n:2]
+    y[..., 0:2 * n:2] = even * c - odd * s
+    y[..., 1:2 * n:2] = even * s + odd * c
+    return y
+
+
+# --- Softmax attention -------------------------------------------------------
+# Causal attention: every token attends to all earlier tokens (global) or to
+# the last W tokens only (local).  "Gemma 4多模态大模型架构详解", section
+# "交错层（局部与全局注意力）".
+
+def masked_softmax_attention(q_rot, q_pos, k_rot, values, k_pos, scale: float,
+                             window: int) -> np.ndarray:
+    """One head: rows of q_rot [Sq, d] at q_pos against keys k_rot [Sk, d] at k_pos.
+
+    Key j is visible to query i when k_pos[j] <= q_pos[i] and, for window > 0,
+    k_pos[j] > q_pos[i] - window.  Softmax over the visible keys.
+    """
+    q_rot, k_rot, values = _f64(q_rot), _f64(k_rot), _f64(values)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    scores = scale * (q_rot @ k_rot.T)
+    visible = k_pos[None, :] <= q_pos[:, None]
+    if window > 0:
+        visible &= k_pos[None, :] > q_pos[:, None] - window
+    if not visible.any(axis=1).all():
+        raise ValueError("a query row has no visible key")
+    scores = np.where(visible, scores, -np.inf)
+    scores = scores - scores.max(axis=1, keepdims=True)
+    weights = np.exp(scores)
+    weights /= weights.sum(axis=1, keepdims=True)
+    return weights @ values
+
+
+# --- The layer ---------------------------------------------------------------
+
+def _check_shapes(layer: OracleLayer, q, k, v):
+    B, S, Hq, d = q.shape
+    if Hq != layer.n_q_heads or d != layer.head_dim:
+        raise ValueError("q shape does not match the layer")
+    if k.shape != (B, S, layer.n_kv_heads, d):
+        raise ValueError("k shape does not match the layer")
+    if layer.kv_shared:
+        if v is not None:
+            raise ValueError("K=V layer takes no separate v")
+    elif v is None or v.shape != k.shape:
+        raise ValueError("local layer needs v shaped like k")
+    return B, S, Hq, d
+
+
+def prefill(layer: OracleLayer, q, k, v, g_q, g_k, rows=None,
+            row_block: int = 512) -> np.ndarray:
+    """Attention output for a whole prompt.
+
+    q [B,S,Hq,d], k [B,S,Hkv,d] and v [B,S,Hkv,d] (None for K=V) are the raw
+    post-projection tensors.  Returns out [B, len(rows), Hq, d] for the query
+    positions ``rows`` (all positions by default).  Rows are evaluated
+    ``row_block`` at a time; each row is its own softmax, so this is the
+    definition evaluated row by row.
+    """
+    B, S, Hq, d = _check_shapes(layer, q, k, v)
+    G = layer.group
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    positions = np.arange(S)
+
+    k_hat = qk_norm(k, g_k, layer.norm_eps)                          # [B,S,Hkv,d]
+    k_rot = rotate(k_hat, positions[None, :, None], layer.rope_theta,
+                   layer.rope_fraction)
+    values = k_hat if layer.kv_shared else _f64(v)
+
+    out = np.empty((B, rows.size, Hq, d), dtype=np.float64)
+    for start in range(0, rows.size, row_block):
+        r = rows[start:start + row_block]
+        q_hat = qk_norm(q[:, r], g_q, layer.norm_eps)                # [B,r,Hq,d]
+        q_rot = rotate(q_hat, r[None, :, None], layer.rope_theta,
+                       layer.rope_fraction)
+        lo = 0 if layer.window == 0 else max(0, int(r.min()) - layer.window + 1)
+        hi = int(r.max()) + 1
+        kp = positions[lo:hi]
+        for b in range(B):
+            for h in range(Hq):
+                c = h // G
+                out[b, start:start + r.size, h] = masked_softmax_attention(
+                    q_rot[b, :, h], r, k_rot[b, lo:hi, c], values[b, lo:hi, c],
+                    kp, layer.scale, layer.window)
+    return out
+
+
+# --- Caches ------------------------------------------------------------------
+# Global layers: one tensor serves as keys and values, stored normalised and
+# unrotated; p-RoPE is applied when the scores are formed.  Local layers: a
+# ring of W slots for the normalised, rotated key and the raw value.
+
+def expected_caches_after_prefill(layer: OracleLayer, k, v, g_k, cache_cap: int):
+    """Cache contents [B,Hkv,cap,d] after a prompt of S tokens (unwritten = nan)."""
+    k = _f64(k)
+    B, S, Hkv, d = k.shape
+    k_hat = qk_norm(k, g_k, layer.norm_eps)
+    kc = np.full((B, Hkv, cache_cap, d), np.nan)
+    if layer.kv_shared:
+        if S > cache_cap:
+            raise ValueError("prompt longer than the cache")
+        kc[:, :, :S] = k_hat.transpose(0, 2, 1, 3)
+        return kc, None
+    if cache_cap != layer.window:
+        raise ValueError("a local cache has exactly W slots")
+    positions = np.arange(S)
+    k_rot = rotate(k_hat, positions[None, :, None], layer.rope_theta,
+                   layer.rope_fraction)
+    vc = np.full_like(kc, np.nan)
+    for p in range(max(0, S - cache_cap), S):
+        kc[:, :, p % cache_cap] = k_rot[:, p]
+        vc[:, :, p % cache_cap] = _f64(v)[:, p]
+    return kc, vc
+
+
+def expected_caches_after_append(layer: OracleLayer, k_cache, v_cache, k_new,
+                                 v_new, g_k, positions):
+    """Write one new token per sequence (k_new [B,Hkv,d]) at ``positions[b]``."""
+    kc = _f64(k_cache).copy()
+    vc = None if v_cache is None else _f64(v_cache).copy()
+    k_hat = qk_norm(k_new, g_k, layer.norm_eps)                      # [B,Hkv,d]
+    cap = kc.shape[2]
+    for b, p in enumerate(np.asarray(positions, dtype=np.int64)):
+        if layer.kv_shared:
+            kc[b, :, p] = k_hat[b]
+        else:
+            kc[b, :, p % cap] = rotate(k_hat[b], p, layer.rope_theta,
+                                       layer.rope_fraction)
+            vc[b, :, p % cap] = _f64(v_new)[b]
+    return kc, vc
+
+
+def decode_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
+                      batches=None) -> np.ndarray:
+    """One decode step per sequence: q [B,Hq,d] raw, query position L_b - 1.
+
+    ``seq_lens[b]`` counts the valid keys including the new token.  Global
+    layers read slots 0..L_b-1 of the K=V cache (slot j = position j) and rotate
+    them on the fly; local layers read the min(L_b, W) filled ring slots, whose
+    keys are stored already rotated.  Returns out [len(batches), Hq, d].
+    """
+    G = layer.group
+    batches = range(q.shape[0]) if batches is None else batches
+    out = []
+    for b in batches:
+        L = int(seq_lens[b])
+        qpos = np.array([L - 1])
+        q_hat = qk_norm(q[b], g_q, layer.norm_eps)                  # [Hq,d]
+        q_rot = rotate(q_hat, L - 1, layer.rope_theta, layer.rope_fraction)
+        rows = np.empty((layer.n_q_heads, layer.head_dim))
+        if layer.kv_shared:
+            kpos = np.arange(L)
+            for h in range(layer.n_q_heads):
+                keys = _f64(k_cache[b, h // G, :L])
+                k_rot = rotate(keys, kpos, layer.rope_theta, layer.rope_fraction)
+                rows[h] = masked_softmax_attention(q_rot[h:h + 1], qpos, k_rot,
+                                                   keys, kpos, layer.scale, 0)[0]
+        else:
+            n = min(L, layer.window)
+            # Slot s holds the latest position congruent to s mod W; all of the
+            # n filled slots lie inside the window of the query at L - 1.
+            kpos = np.array([L - 1 - ((L - 1 - s) % layer.window) for s in range(n)])
+            for h in range(layer.n_q_heads):
+                rows[h] = masked_softmax_attention(
+                    q_rot[h:h + 1], qpos, k_cache[b, h // G, :n],
+                    v_cache[b, h // G, :n], kpos, layer.scale, layer.window)[0]
+        out.append(rows)
+    return np.stack(out)
+
+
+def cache_bytes_per_token(head_dim: int, fraction: float, layout: str,
+                          bytes_per_elem: float = 1.0) -> float:
+    """Bytes one KV head caches per token under three global-layer layouts.
+
+    ``separate``: K and V, 2d.  ``prerotated``: the rotated p*d dims of K plus the
+    unrotated d dims used as V, (1+p)*d.  ``shared``: one unrotated K=V tensor, d
+    (p-RoPE applied when the scores are formed).
+    """
+    if layout == "separate":
+        n = 2 * head_dim
+    elif layout == "prerotated":
+        n = head_dim + 2 * rotated_pairs(head_dim, fraction)
+    elif layout == "shared":
+        n = head_dim
+    else:
+        raise ValueError(layout)
+    return n * bytes_per_elem
