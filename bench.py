@@ -1,0 +1,202 @@
+"""Benchmark: global K=V attention prefill at 32K (TFLOP/s) and global K=V decode
+(KV GB/s), each against the MI355X roofline, with the float64 oracle timed on
+the host as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  A step is one pass of the hot path over the workload:
+one gemma_attn_prefill call (RoPE table + key/value prep + attention) on the
+32K global-layer prefill.  The decode measurement (one gemma_attn_decode call
+on 16 sequences with lengths drawn from [4096, 131072]) is reported beside it.
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+MI355X_BF16_DENSE_TFLOPS = 2500.0   # published dense bf16 MFMA peak
+MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def bench_prefill(args, torch, api, W):
+    wl = W.CONFIGS["global_prefill_32k"]
+    shape, S = wl.layer, wl.seq_len
+    dev = torch.device("cuda", 0)
+    x = wl.draw(dev)
+    lay = api.Layer.from_shape(shape, torch.bfloat16)
+    kc = torch.empty((1, shape.n_kv_heads, S, shape.head_dim), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(x["q"])
+    ws = api.workspace(api.gemma_attn_prefill_workspace_size(lay, 1, S), dev)
+
+    def step():
+        api.gemma_attn_prefill(lay, x["q"], x["k"], None, x["g_q"], x["g_k"], kc, None, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    sec = timed(step, args.steps, 0, torch)
+    api.profile_enable(False)
+    attn_ms, n_attn = api.profile_read("prefill_attn")
+    prep_ms, n_prep = api.profile_read("prefill_prep")
+    api.profile_reset()
+    flops = wl.flops()
+    return {
+        "sec": sec, "flops": flops, "attn_ms": attn_ms / max(n_attn, 1), "prep_ms": prep_ms / max(n_prep, 1),
+        "n_attn": n_attn, "wl": wl, "x": x,
+    }
+
+
+def bench_decode(args, torch, api, W):
+    wl = W.CONFIGS["global_decode"]
+    shape = wl.layer
+    dev = torch.device("cuda", 0)
+    lens = wl.lengths()
+    B, cap, D = wl.batch, wl.cache_cap(), shape.head_dim
+    kc = W.normal((B, shape.n_kv_heads, cap, D), wl.seed, "k_cache", torch.bfloat16, dev)
+    q = W.normal((B, shape.n_q_heads, D), wl.seed, "q_dec", torch.bfloat16, dev)
+    g_q = W.gains(D, wl.seed, "g_q", False, torch.bfloat16, dev)
+    lay = api.Layer.from_shape(shape, torch.bfloat16)
+    seq = lens.to(dev)
+    maxlen = int(lens.max())
+    out = torch.empty_like(q)
+    ws = api.workspace(api.gemma_attn_decode_workspace_size(lay, B, maxlen), dev)
+
+    def step():
+        api.gemma_attn_decode(lay, q, g_q, kc, None, seq, maxlen, out, ws)
+
+    steps = args.decode_steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    sec = timed(step, steps, 0, torch)
+    api.profile_enable(False)
+    split_ms, n_split = api.profile_read("decode_splitk")
+    merge_ms, n_merge = api.profile_read("decode_merge")
+    api.profile_reset()
+    nbytes = wl.kv_bytes(lens)
+    del kc
+    torch.cuda.empty_cache()
+    return {"sec": sec, "bytes": nbytes, "split_ms": split_ms / max(n_split, 1),
+            "merge_ms": merge_ms / max(n_merge, 1), "lens": lens}
+
+
+def cpu_baseline(pre, budget_s, torch):
+    """The oracle as it stands, on a bounded sample of the same prefill."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    wl, x = pre["wl"], pre["x"]
+    shape = wl.layer
+    ol = O.OracleLayer(shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.window, shape.kv_shared,
+                       shape.rope_theta, shape.rope_fraction, shape.norm_eps)
+    S = wl.seq_len
+    rng = np.random.default_rng(0)
+    k64 = x["k"].to("cpu", torch.float64).numpy()
+    g_q = x["g_q"].to("cpu", torch.float64).numpy()
+    g_k = x["g_k"].to("cpu", torch.float64).numpy()
+    done_rows, flops, elapsed = 0, 0.0, 0.0
+    t0 = time.perf_counter()
+    while elapsed < budget_s and done_rows < 256:
+        rows = np.sort(rng.integers(0, S, size=4))
+        q_rows = x["q"][:, torch.as_tensor(rows, device=x["q"].device)].to("cpu", torch.float64).numpy()
+        hi = int(rows.max()) + 1
+        O.prefill(ol, q_rows, k64[:, :hi], None, g_q, g_k, rows=rows, q_at_rows=True)
+        done_rows += len(rows)
+        flops += 4.0 * shape.n_q_heads * shape.head_dim * float(np.sum(rows + 1))
+        elapsed = time.perf_counter() - t0
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done_rows} random query rows of the same 32K global prefill (all 32 heads), "
+                      f"float64 numpy, {elapsed:.1f} s incl. key norm/rotation per call"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a single "
+              "MI355X and has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from global_gqa_rope_amd import api
+    from global_gqa_rope_amd import workloads as W
+
+    pre = bench_prefill(args, torch, api, W)
+    tflops = pre["flops"] / pre["sec"] / 1e12
+    attn_tflops = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "global K=V attn prefill TFLOP/s @32K; decode KV GB/s (% of MI355X roofline)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["sec"] * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k, QKNorm gains N(1,0.1))",
+        "config": {"workload": "global K=V layer prefill: B=1, S=32768, 32 query heads / 4 K=V heads, "
+                               "d=512, causal, p-RoPE p=0.25 theta=1e6, QKNorm",
+                   "batch": 1, "seq_len": 32768, "flops_per_step": pre["flops"]},
+        "roofline": {"kernel": "prefill_attn_kernel<bf16,512,8>", "bound": "mfma",
+                     "achieved": round(attn_tflops, 2), "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None,
+                     "avg_ms": round(pre["attn_ms"], 4), "prep_avg_ms": round(pre["prep_ms"], 4)},
+    }
+    if not args.no_decode:
+        dec = bench_decode(args, torch, api, W)
+        gbs = dec["bytes"] / dec["sec"] / 1e9
+        split_gbs = dec["bytes"] / (dec["split_ms"] * 1e-3) / 1e9
+        line["decode"] = {
+            "workload": "global K=V layer decode: B=16, context ~ U[4096,131072] (seed 0), 32q/4kv, d=512",
+            "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(dec["sec"] * 1e3, 4),
+            "kv_bytes": dec["bytes"],
+            "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V>", "bound": "hbm",
+                         "achieved": round(split_gbs, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                         "frac": round(split_gbs / MI355X_HBM_GBS, 4), "traffic": None,
+                         "avg_ms": round(dec["split_ms"], 4), "merge_avg_ms": round(dec["merge_ms"], 4)},
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds, torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

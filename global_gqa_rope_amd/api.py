@@ -1,0 +1,169 @@
+"""Torch-facing binding of the C ABI: argument marshalling only.
+
+Every function here checks tensor devices, dtypes and shapes, passes raw
+device pointers and the current HIP stream to libgemma_attn.so, and raises
+GemmaAttnError on a non-OK status.  No step of the computation runs here.
+Names follow the C entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import GaLayer, GemmaAttnError  # noqa: F401
+
+_DTYPES = {torch.bfloat16: _lib.GA_BF16, torch.float32: _lib.GA_F32}
+
+
+@dataclass(frozen=True)
+class Layer:
+    """Python mirror of ga_layer."""
+
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    window: int
+    kv_shared: bool
+    rope_theta: float
+    rope_fraction: float
+    norm_eps: float = 1e-6
+    softmax_scale: float = 0.0     # <= 0: 1/sqrt(head_dim)
+    dtype: torch.dtype = torch.bfloat16
+
+    def struct(self) -> GaLayer:
+        return GaLayer(self.n_q_heads, self.n_kv_heads, self.head_dim, self.window,
+                       int(self.kv_shared), self.rope_theta, self.rope_fraction, self.norm_eps,
+                       self.softmax_scale, _DTYPES[self.dtype])
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return self.softmax_scale if self.softmax_scale > 0 else 1.0 / math.sqrt(self.head_dim)
+
+    @staticmethod
+    def from_shape(shape, dtype: torch.dtype, softmax_scale: float = 0.0) -> "Layer":
+        return Layer(shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.window,
+                     shape.kv_shared, shape.rope_theta, shape.rope_fraction, shape.norm_eps,
+                     softmax_scale, dtype)
+
+
+def _ptr(t: torch.Tensor | None, name: str, layer: Layer | None = None, shape=None,
+         dtype=None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    want = dtype if dtype is not None else (layer.dtype if layer is not None else None)
+    if want is not None and t.dtype != want:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {want}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def gemma_attn_prefill_workspace_size(layer: Layer, batch: int, seq_len: int) -> int:
+    return int(_lib.load().gemma_attn_prefill_workspace_size(ctypes.byref(layer.struct()), batch, seq_len))
+
+
+def gemma_attn_decode_workspace_size(layer: Layer, batch: int, max_seq_len: int) -> int:
+    return int(_lib.load().gemma_attn_decode_workspace_size(ctypes.byref(layer.struct()), batch, max_seq_len))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """Caller-owned scratch (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def gemma_attn_prefill(layer: Layer, q, k, v, q_gain, k_gain, k_cache=None, v_cache=None,
+                       out=None, ws=None, stream=None) -> torch.Tensor:
+    B, S, Hq, d = q.shape
+    Hkv = layer.n_kv_heads
+    if out is None:
+        out = torch.empty_like(q)
+    need = gemma_attn_prefill_workspace_size(layer, B, S)
+    if ws is None:
+        ws = workspace(need, q.device)
+    cap = 0 if k_cache is None else k_cache.shape[2]
+    if k_cache is not None:
+        _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d))
+    if v_cache is not None:
+        _ptr(v_cache, "v_cache", layer, (B, Hkv, cap, d))
+    st = _lib.load().gemma_attn_prefill(
+        ctypes.byref(layer.struct()), B, S,
+        _ptr(q, "q", layer, (B, S, Hq, d)), _ptr(k, "k", layer, (B, S, Hkv, d)),
+        _ptr(v, "v", layer, (B, S, Hkv, d)), _ptr(q_gain, "q_gain", layer, (d,)),
+        _ptr(k_gain, "k_gain", layer, (d,)), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+        cap, _ptr(out, "out", layer, (B, S, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8),
+        ws.numel(), _stream(stream))
+    _lib.check(st)
+    return out
+
+
+def kv_append(layer: Layer, k_new, v_new, k_gain, positions, k_cache, v_cache=None,
+              stream=None) -> None:
+    B, Hkv, d = k_new.shape
+    cap = k_cache.shape[2]
+    st = _lib.load().kv_append(
+        ctypes.byref(layer.struct()), B, _ptr(k_new, "k_new", layer, (B, Hkv, d)),
+        _ptr(v_new, "v_new", layer, (B, Hkv, d)), _ptr(k_gain, "k_gain", layer, (d,)),
+        _ptr(positions, "positions", dtype=torch.int32, shape=(B,)),
+        _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d)),
+        _ptr(v_cache, "v_cache", layer, (B, Hkv, cap, d)), cap, _stream(stream))
+    _lib.check(st)
+
+
+def gemma_attn_decode(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens, max_seq_len: int,
+                      out=None, ws=None, stream=None) -> torch.Tensor:
+    B, Hq, d = q.shape
+    Hkv = layer.n_kv_heads
+    cap = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(gemma_attn_decode_workspace_size(layer, B, max_seq_len), q.device)
+    st = _lib.load().gemma_attn_decode(
+        ctypes.byref(layer.struct()), B, _ptr(q, "q", layer, (B, Hq, d)),
+        _ptr(q_gain, "q_gain", layer, (d,)), _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d)),
+        _ptr(v_cache, "v_cache", layer, (B, Hkv, cap, d)), cap,
+        _ptr(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,)), int(max_seq_len),
+        _ptr(out, "out", layer, (B, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8), ws.numel(),
+        _stream(stream))
+    _lib.check(st)
+    return out
+
+
+# ---- kernel timing hooks ------------------------------------------------------
+KERNEL_IDS = {"prefill_attn": 0, "prefill_prep": 1, "decode_splitk": 2, "decode_merge": 3,
+              "kv_append": 4}
+
+
+def profile_enable(on: bool = True) -> None:
+    _lib.load().gemma_attn_profile_enable(1 if on else 0)
+
+
+def profile_reset() -> None:
+    _lib.load().gemma_attn_profile_reset()
+
+
+def profile_read(kernel: str) -> tuple[float, int]:
+    """(total ms, launch count) of one kernel since the last reset."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int()
+    if _lib.load().gemma_attn_profile_read(KERNEL_IDS[kernel], ctypes.byref(ms), ctypes.byref(n)) != 0:
+        raise RuntimeError("reading the kernel timing events failed")
+    return ms.value, n.value

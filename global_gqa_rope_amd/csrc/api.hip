@@ -1,0 +1,336 @@
+// C ABI: argument validation, workspace layout and kernel dispatch.
+// Validation runs entirely on the host before any HIP call, so every error
+// path is exercised without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/gemma_attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+ga_status fail(ga_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+ga_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GA_OK;
+  return fail(GA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- kernel timing hooks -----------------------------------------------------
+// When enabled, a pair of HIP events brackets every attention / decode kernel
+// launch on the caller's stream; gemma_attn_profile_read() resolves them.
+struct Timed {
+  int kernel;   // 0 prefill attention, 1 prefill prep, 2 decode split-K, 3 decode merge, 4 kv_append
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Timed> g_prof;
+
+struct ProfScope {
+  hipStream_t s;
+  int kernel;
+  hipEvent_t start = nullptr, stop = nullptr;
+  ProfScope(hipStream_t st, int k) : s(st), kernel(k) {
+    if (!g_prof_on) return;
+    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess) {
+      start = stop = nullptr;
+      return;
+    }
+    hipEventRecord(start, s);
+  }
+  ~ProfScope() {
+    if (!start) return;
+    hipEventRecord(stop, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({kernel, start, stop});
+  }
+};
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Derived {
+  int group;
+  int n_rot;
+  int elem;
+  float scale;
+  double log2_theta;
+};
+
+// Validity first (GA_EINVAL), then what the built kernels cover (GA_EUNSUPPORTED).
+ga_status check_layer(const ga_layer* L, Derived* out) {
+  if (!L) return fail(GA_EINVAL, "layer is NULL");
+  if (L->n_q_heads <= 0 || L->n_kv_heads <= 0 || L->head_dim <= 0)
+    return fail(GA_EINVAL, "head counts and head_dim must be positive");
+  if (L->n_q_heads % L->n_kv_heads)
+    return fail(GA_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", L->n_q_heads, L->n_kv_heads);
+  if (L->head_dim % 2) return fail(GA_EINVAL, "head_dim must be even");
+  if (L->window < 0) return fail(GA_EINVAL, "window must be >= 0");
+  if (L->kv_shared != 0 && L->kv_shared != 1) return fail(GA_EINVAL, "kv_shared must be 0 or 1");
+  if (!(L->rope_theta > 0.f) || !std::isfinite(L->rope_theta)) return fail(GA_EINVAL, "rope_theta must be > 0");
+  if (!(L->rope_fraction >= 0.f && L->rope_fraction <= 1.f))
+    return fail(GA_EINVAL, "rope_fraction must lie in [0, 1]");
+  const double pairs = static_cast<double>(L->rope_fraction) * L->head_dim / 2.0;
+  const double rounded = std::nearbyint(pairs);
+  if (std::fabs(pairs - rounded) > 1e-6)
+    return fail(GA_EINVAL, "rope_fraction * head_dim / 2 = %g is not a whole number of pairs", pairs);
+  if (!(L->norm_eps > 0.f)) return fail(GA_EINVAL, "norm_eps must be > 0");
+  if (!std::isfinite(L->softmax_scale)) return fail(GA_EINVAL, "softmax_scale must be finite");
+  if (L->dtype != GA_BF16 && L->dtype != GA_F32) return fail(GA_EINVAL, "dtype must be GA_BF16 or GA_F32");
+
+  const int G = L->n_q_heads / L->n_kv_heads;
+  const int n_rot = static_cast<int>(rounded);
+  if (L->head_dim != 256 && L->head_dim != 512)
+    return fail(GA_EUNSUPPORTED, "head_dim %d: kernels are built for 256 and 512", L->head_dim);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(GA_EUNSUPPORTED, "n_q_heads / n_kv_heads = %d: kernels are built for 1, 2, 4, 8", G);
+  if (L->kv_shared && L->window > 0)
+    return fail(GA_EUNSUPPORTED, "K=V layers are supported with window 0 only");
+  if (L->kv_shared && n_rot != 64)
+    return fail(GA_EUNSUPPORTED, "K=V layers rotate exactly 64 pairs on the fly (got %d)", n_rot);
+  if (out) {
+    out->group = G;
+    out->n_rot = n_rot;
+    out->elem = L->dtype == GA_BF16 ? 2 : 4;
+    out->scale = L->softmax_scale > 0.f ? L->softmax_scale : 1.0f / std::sqrt(static_cast<float>(L->head_dim));
+    out->log2_theta = std::log2(static_cast<double>(L->rope_theta));
+  }
+  return GA_OK;
+}
+
+// Cache arguments shared by prefill and kv_append.
+ga_status check_caches(const ga_layer* L, const void* k_cache, const void* v_cache, int32_t cache_cap,
+                       bool optional, int32_t min_cap) {
+  if (!k_cache) {
+    if (!optional) return fail(GA_EINVAL, "k_cache is NULL");
+    if (v_cache) return fail(GA_EINVAL, "v_cache given without k_cache");
+    return GA_OK;
+  }
+  if (cache_cap <= 0) return fail(GA_EINVAL, "cache_cap must be > 0");
+  if (L->kv_shared) {
+    if (v_cache) return fail(GA_EINVAL, "K=V layer: v_cache must be NULL (one cache tensor)");
+  } else if (!v_cache) {
+    return fail(GA_EINVAL, "layer with a separate V needs v_cache");
+  }
+  if (L->window > 0) {
+    if (cache_cap != L->window)
+      return fail(GA_EINVAL, "windowed layer: cache_cap (%d) must equal window (%d)", cache_cap, L->window);
+  } else if (cache_cap < min_cap) {
+    return fail(GA_EINVAL, "cache_cap (%d) is smaller than the sequence (%d)", cache_cap, min_cap);
+  }
+  return GA_OK;
+}
+
+struct PrefillLayout {
+  size_t table, ws_k, ws_vt, total;
+  int seq_pad;
+};
+
+PrefillLayout prefill_layout(const ga_layer* L, const Derived& dv, int batch, int seq_len) {
+  PrefillLayout p;
+  p.seq_pad = (seq_len + ga::kPrepTile - 1) / ga::kPrepTile * ga::kPrepTile;
+  const size_t kv = static_cast<size_t>(batch) * L->n_kv_heads * p.seq_pad * L->head_dim * dv.elem;
+  p.table = 0;
+  p.ws_k = align_up(static_cast<size_t>(p.seq_pad) * dv.n_rot * 8);
+  p.ws_vt = p.ws_k + align_up(kv);
+  p.total = p.ws_vt + align_up(kv);
+  return p;
+}
+
+int decode_chunks(const ga_layer* L, int max_seq_len) {
+  const int keys = L->window > 0 ? std::min(max_seq_len, L->window) : max_seq_len;
+  return (keys + ga::kDecodeChunk - 1) / ga::kDecodeChunk;
+}
+
+size_t decode_bytes(const ga_layer* L, const Derived& dv, int batch, int max_seq_len) {
+  const int n = decode_chunks(L, max_seq_len);
+  if (n <= 1) return 0;
+  return align_up(static_cast<size_t>(batch) * L->n_kv_heads * n * dv.group * (L->head_dim + 2) * 4);
+}
+
+ga_status check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return GA_OK;
+  if (!ws) return fail(GA_EWORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(GA_EINVAL, "workspace must be 256-byte aligned");
+  if (have < need) return fail(GA_EWORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return GA_OK;
+}
+
+}  // namespace
+
+// Decode launches two kernels; the launcher reports each to this callback.
+void record_decode(hipStream_t s, int which, bool before) {
+  static thread_local hipEvent_t pending = nullptr;
+  if (before) {
+    if (hipEventCreate(&pending) == hipSuccess) hipEventRecord(pending, s);
+    else pending = nullptr;
+    return;
+  }
+  if (!pending) return;
+  hipEvent_t stop;
+  if (hipEventCreate(&stop) != hipSuccess) return;
+  hipEventRecord(stop, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back({which, pending, stop});
+  pending = nullptr;
+}
+
+extern "C" {
+
+void gemma_attn_profile_enable(int on) { g_prof_on = on != 0; }
+
+int gemma_attn_profile_read(int kernel, double* total_ms, int* count) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double t = 0.0;
+  int n = 0;
+  for (const Timed& e : g_prof) {
+    if (e.kernel != kernel) continue;
+    if (hipEventSynchronize(e.stop) != hipSuccess) return -1;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess) return -1;
+    t += ms;
+    ++n;
+  }
+  if (total_ms) *total_ms = t;
+  if (count) *count = n;
+  return 0;
+}
+
+void gemma_attn_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const Timed& e : g_prof) {
+    hipEventDestroy(e.start);
+    hipEventDestroy(e.stop);
+  }
+  g_prof.clear();
+}
+
+const char* gemma_attn_last_error(void) { return g_error.c_str(); }
+
+const char* gemma_attn_version(void) { return "gemma_attn 0.1 (gfx950)"; }
+
+size_t gemma_attn_prefill_workspace_size(const ga_layer* layer, int32_t batch, int32_t seq_len) {
+  Derived dv;
+  if (check_layer(layer, &dv) != GA_OK || batch < 0 || seq_len < 0) return 0;
+  return prefill_layout(layer, dv, batch, seq_len).total;
+}
+
+size_t gemma_attn_decode_workspace_size(const ga_layer* layer, int32_t batch, int32_t max_seq_len) {
+  Derived dv;
+  if (check_layer(layer, &dv) != GA_OK || batch < 0 || max_seq_len < 1) return 0;
+  return decode_bytes(layer, dv, batch, max_seq_len);
+}
+
+ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_len, const void* q,
+                             const void* k, const void* v, const void* q_gain, const void* k_gain,
+                             void* k_cache, void* v_cache, int32_t cache_cap, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Derived dv;
+  ga_status st = check_layer(layer, &dv);
+  if (st != GA_OK) return st;
+  if (batch < 0 || seq_len < 0) return fail(GA_EINVAL, "batch and seq_len must be >= 0");
+  if (seq_len > (1 << 22)) return fail(GA_EUNSUPPORTED, "seq_len above 4M positions");
+  if (batch == 0 || seq_len == 0) return GA_OK;
+  if (!q || !k || !q_gain || !k_gain || !out) return fail(GA_EINVAL, "q, k, q_gain, k_gain and out must be non-NULL");
+  if (layer->kv_shared && v) return fail(GA_EINVAL, "K=V layer: v must be NULL (keys are the values)");
+  if (!layer->kv_shared && !v) return fail(GA_EINVAL, "layer with a separate V needs v");
+  st = check_caches(layer, k_cache, v_cache, cache_cap, true, seq_len);
+  if (st != GA_OK) return st;
+  const PrefillLayout lay = prefill_layout(layer, dv, batch, seq_len);
+  st = check_workspace(workspace, workspace_bytes, lay.total);
+  if (st != GA_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  {
+    ProfScope ps(s, 1);
+    st = hip_status(ga::launch_rope_table(ws + lay.table, lay.seq_pad, dv.n_rot, layer->head_dim, dv.log2_theta, s),
+                    "rope table launch");
+    if (st == GA_OK) {
+      ga::PrepArgs pa{};
+      pa.k = k; pa.v = v; pa.k_gain = k_gain; pa.rope_table = ws + lay.table;
+      pa.k_cache = k_cache; pa.v_cache = v_cache; pa.ws_k = ws + lay.ws_k; pa.ws_vt = ws + lay.ws_vt;
+      pa.seq_len = seq_len; pa.seq_pad = lay.seq_pad; pa.n_kv_heads = layer->n_kv_heads; pa.n_rot = dv.n_rot;
+      pa.window = layer->window; pa.kv_shared = layer->kv_shared; pa.cache_cap = cache_cap; pa.eps = layer->norm_eps;
+      st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "prefill prep launch");
+    }
+  }
+  if (st != GA_OK) return st;
+
+  ga::PrefillArgs fa{};
+  fa.q = q; fa.q_gain = q_gain; fa.rope_table = ws + lay.table; fa.ws_k = ws + lay.ws_k; fa.ws_vt = ws + lay.ws_vt;
+  fa.out = out; fa.seq_len = seq_len; fa.seq_pad = lay.seq_pad; fa.n_q_heads = layer->n_q_heads;
+  fa.n_kv_heads = layer->n_kv_heads; fa.n_rot = dv.n_rot; fa.window = layer->window; fa.eps = layer->norm_eps;
+  fa.qk_scale_log2 = dv.scale * 1.4426950408889634f;
+  ProfScope ps(s, 0);
+  return hip_status(ga::launch_prefill_attn(fa, layer->dtype, layer->head_dim, dv.group, batch, s),
+                    "prefill attention launch");
+}
+
+ga_status kv_append(const ga_layer* layer, int32_t batch, const void* k_new, const void* v_new,
+                    const void* k_gain, const int32_t* positions, void* k_cache, void* v_cache,
+                    int32_t cache_cap, void* stream) {
+  Derived dv;
+  ga_status st = check_layer(layer, &dv);
+  if (st != GA_OK) return st;
+  if (batch < 0) return fail(GA_EINVAL, "batch must be >= 0");
+  if (batch == 0) return GA_OK;
+  if (!k_new || !k_gain || !positions) return fail(GA_EINVAL, "k_new, k_gain and positions must be non-NULL");
+  if (layer->kv_shared && v_new) return fail(GA_EINVAL, "K=V layer: v_new must be NULL");
+  if (!layer->kv_shared && !v_new) return fail(GA_EINVAL, "layer with a separate V needs v_new");
+  st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
+  if (st != GA_OK) return st;
+  ga::AppendArgs aa{};
+  aa.k_new = k_new; aa.v_new = v_new; aa.k_gain = k_gain; aa.positions = positions;
+  aa.k_cache = k_cache; aa.v_cache = v_cache; aa.n_kv_heads = layer->n_kv_heads; aa.n_rot = dv.n_rot;
+  aa.window = layer->window; aa.kv_shared = layer->kv_shared; aa.cache_cap = cache_cap; aa.eps = layer->norm_eps;
+  aa.log2_theta = dv.log2_theta;
+  ProfScope ps(static_cast<hipStream_t>(stream), 4);
+  return hip_status(ga::launch_kv_append(aa, layer->dtype, layer->head_dim, batch, static_cast<hipStream_t>(stream)),
+                    "kv_append launch");
+}
+
+ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q, const void* q_gain,
+                            const void* k_cache, const void* v_cache, int32_t cache_cap,
+                            const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  Derived dv;
+  ga_status st = check_layer(layer, &dv);
+  if (st != GA_OK) return st;
+  if (batch < 0) return fail(GA_EINVAL, "batch must be >= 0");
+  if (batch == 0) return GA_OK;
+  if (max_seq_len < 1) return fail(GA_EINVAL, "max_seq_len must be >= 1");
+  if (!q || !q_gain || !seq_lens || !out) return fail(GA_EINVAL, "q, q_gain, seq_lens and out must be non-NULL");
+  st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
+  if (st != GA_OK) return st;
+  const size_t need = decode_bytes(layer, dv, batch, max_seq_len);
+  st = check_workspace(workspace, workspace_bytes, need);
+  if (st != GA_OK) return st;
+  ga::DecodeArgs da{};
+  da.q = q; da.q_gain = q_gain; da.k_cache = k_cache; da.v_cache = v_cache; da.seq_lens = seq_lens;
+  da.out = out; da.partials = static_cast<float*>(workspace); da.n_q_heads = layer->n_q_heads;
+  da.n_kv_heads = layer->n_kv_heads; da.n_rot = dv.n_rot; da.window = layer->window; da.cache_cap = cache_cap;
+  da.max_seq_len = max_seq_len; da.n_chunks = decode_chunks(layer, max_seq_len); da.eps = layer->norm_eps;
+  da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
+  return hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
+                                      static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),
+                    "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,251 @@
+// Key/value preparation kernels: the RoPE angle table, the prefill K/V pass
+// (QKNorm, rotation, transposed value tiles, cache fill) and kv_append.
+#include "common.h"
+#include "kernels.h"
+
+namespace ga {
+
+// table[pos][pair] = (cos, sin)(pos * theta^(-2 pair / d)), fp64 math.
+__global__ void rope_table_kernel(f32x2* __restrict__ table, int n_pos, int n_rot,
+                                  int head_dim, double log2_theta) {
+  const int64_t total = static_cast<int64_t>(n_pos) * n_rot;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int pos = static_cast<int>(i / n_rot);
+    const int pair = static_cast<int>(i % n_rot);
+    table[i] = rope_cos_sin(static_cast<double>(pos) * rope_omega(pair, head_dim, log2_theta));
+  }
+}
+
+// One workgroup per (tile of kPrepTile key positions, kv head, batch).
+// Thread t owns key row r = t / 8 of the tile and the 8-element chunks
+// i * 8 + t % 8 of that row, so eight neighbouring lanes cover 64 contiguous
+// elements of one row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
+  constexpr int kChunks = D / 8;             // 8-element chunks per row
+  constexpr int kMine = kChunks / 8;         // chunks per thread
+  __shared__ __attribute__((aligned(16))) T vtile[kPrepTile][D];
+
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x;
+  const int r = t >> 3, c8 = t & 7;
+  const int pos = tile * kPrepTile + r;
+  const bool valid = pos < a.seq_len;
+  // padding positions read the last real row (then zeroed) so no load leaves the tensor
+  const int src_pos = valid ? pos : a.seq_len - 1;
+  const int64_t src_row = ((static_cast<int64_t>(b) * a.seq_len + src_pos) * a.n_kv_heads + h) * D;
+
+  const T* __restrict__ k = static_cast<const T*>(a.k);
+  const T* __restrict__ v = static_cast<const T*>(a.v);
+  const T* __restrict__ gk = static_cast<const T*>(a.k_gain);
+
+  float x[kMine][8];
+#pragma unroll
+  for (int i = 0; i < kMine; ++i) {
+    const int d0 = (i * 8 + c8) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[i][j] = valid ? to_f32(k[src_row + d0 + j]) : 0.f;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMine; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += x[i][j] * x[i][j];
+  ss += wave_xor(ss, 1);
+  ss += wave_xor(ss, 2);
+  ss += wave_xor(ss, 4);
+  const float rstd = 1.0f / sqrtf(ss / D + a.eps);
+#pragma unroll
+  for (int i = 0; i < kMine; ++i) {
+    const int d0 = (i * 8 + c8) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[i][j] = x[i][j] * rstd * to_f32(gk[d0 + j]);
+  }
+
+  const int64_t head_base = (static_cast<int64_t>(b) * a.n_kv_heads + h);
+  T* __restrict__ kc = static_cast<T*>(a.k_cache);
+  T* __restrict__ vc = static_cast<T*>(a.v_cache);
+
+  // K=V: the cache keeps the normalised, unrotated key; it is also the value.
+  if (a.kv_shared) {
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int d0 = (i * 8 + c8) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vtile[r][d0 + j] = from_f32<T>(x[i][j]);
+      if (kc && valid) {
+        T* dst = kc + (head_base * a.cache_cap + pos) * D + d0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[j] = from_f32<T>(x[i][j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int d0 = (i * 8 + c8) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vtile[r][d0 + j] = valid ? v[src_row + d0 + j] : from_f32<T>(0.f);
+    }
+  }
+
+  // Rotate the first 2*n_rot dims.
+  const f32x2* __restrict__ table = static_cast<const f32x2*>(a.rope_table);
+#pragma unroll
+  for (int i = 0; i < kMine; ++i) {
+    const int d0 = (i * 8 + c8) * 8;
+    if (d0 < 2 * a.n_rot && valid) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pair = d0 / 2 + j;
+        if (pair < a.n_rot)
+          rotate_pair(x[i][2 * j], x[i][2 * j + 1], table[static_cast<int64_t>(pos) * a.n_rot + pair]);
+      }
+    }
+  }
+
+  // Rotated keys into the operand-ordered key tile (padded rows zero).  Chunk c
+  // of row r is fragment c/2, lane r + 32 (c & 1).
+  const int64_t tile_base = (head_base * (a.seq_pad / kPrepTile) + tile) * (kPrepTile * D);
+  {
+    char* kt = reinterpret_cast<char*>(static_cast<T*>(a.ws_k) + tile_base);
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int c = i * 8 + c8;
+      char* frag = kt + (c >> 1) * frag_bytes<T>();
+      const int ln = r + 32 * (c & 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<T*>(frag + frag_elem_off<T>(ln, j)) = from_f32<T>(x[i][j]);
+    }
+  }
+
+  // Windowed layers: the ring keeps the last W positions, keys rotated.
+  if (!a.kv_shared && a.window > 0 && kc && valid && pos >= a.seq_len - a.window) {
+    const int slot = pos % a.cache_cap;
+    T* dk = kc + (head_base * a.cache_cap + slot) * D;
+    T* dv = vc + (head_base * a.cache_cap + slot) * D;
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int d0 = (i * 8 + c8) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        dk[d0 + j] = from_f32<T>(x[i][j]);
+        dv[d0 + j] = v[src_row + d0 + j];
+      }
+    }
+  }
+  // Global layers with a separate V: slot = position.
+  if (!a.kv_shared && a.window == 0 && kc && valid) {
+    T* dk = kc + (head_base * a.cache_cap + pos) * D;
+    T* dv = vc + (head_base * a.cache_cap + pos) * D;
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int d0 = (i * 8 + c8) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        dk[d0 + j] = from_f32<T>(x[i][j]);
+        dv[d0 + j] = v[src_row + d0 + j];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Values into the operand-ordered value tile: column d of the staged tile
+  // goes to fragments 2 (d / 32) + s, lanes d % 32 + 32 g.
+  {
+    char* vt = reinterpret_cast<char*>(static_cast<T*>(a.ws_vt) + tile_base);
+    for (int d = t; d < D; d += 256) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          char* frag = vt + (2 * (d / 32) + s) * frag_bytes<T>();
+          const int ln = (d & 31) + 32 * g;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<T*>(frag + frag_elem_off<T>(ln, j)) = vtile[key_perm(16 * s + 8 * g + j)][d];
+        }
+      }
+    }
+  }
+}
+
+// One wave per (kv head, batch).  Lane l owns dims [l*D/64, (l+1)*D/64).
+template <typename T, int D>
+__global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
+  constexpr int kPer = D / 64;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int l = threadIdx.x;
+  const int pos = a.positions[b];
+  const int64_t head_base = static_cast<int64_t>(b) * a.n_kv_heads + h;
+  if (pos < 0) return;
+  if (a.kv_shared && pos >= a.cache_cap) return;
+  const int slot = a.window > 0 ? pos % a.cache_cap : pos;
+  if (slot >= a.cache_cap) return;
+
+  const T* __restrict__ kn = static_cast<const T*>(a.k_new) + head_base * D + l * kPer;
+  const T* __restrict__ gk = static_cast<const T*>(a.k_gain) + l * kPer;
+  float x[kPer];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    x[j] = to_f32(kn[j]);
+    ss += x[j] * x[j];
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) ss += wave_xor(ss, m);
+  const float rstd = 1.0f / sqrtf(ss / D + a.eps);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) x[j] = x[j] * rstd * to_f32(gk[j]);
+
+  T* __restrict__ kc = static_cast<T*>(a.k_cache) + (head_base * a.cache_cap + slot) * D + l * kPer;
+  if (!a.kv_shared) {
+#pragma unroll
+    for (int j = 0; j < kPer / 2; ++j) {
+      const int pair = l * kPer / 2 + j;
+      if (pair < a.n_rot)
+        rotate_pair(x[2 * j], x[2 * j + 1],
+                    rope_cos_sin(static_cast<double>(pos) * rope_omega(pair, D, a.log2_theta)));
+    }
+    const T* __restrict__ vn = static_cast<const T*>(a.v_new) + head_base * D + l * kPer;
+    T* __restrict__ vcp = static_cast<T*>(a.v_cache) + (head_base * a.cache_cap + slot) * D + l * kPer;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) vcp[j] = vn[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) kc[j] = from_f32<T>(x[j]);
+}
+
+// ---- launchers ---------------------------------------------------------------
+
+hipError_t launch_rope_table(void* table, int n_pos, int n_rot, int head_dim, double log2_theta,
+                             hipStream_t s) {
+  if (n_rot == 0 || n_pos == 0) return hipSuccess;
+  const int64_t total = static_cast<int64_t>(n_pos) * n_rot;
+  const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 4096));
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, static_cast<f32x2*>(table),
+                     n_pos, n_rot, head_dim, log2_theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_prep(const PrepArgs& a, int dtype, int head_dim, int batch, hipStream_t s) {
+  const dim3 grid(a.seq_pad / kPrepTile, a.n_kv_heads, batch);
+  if (dtype == 0 && head_dim == 512) hipLaunchKernelGGL((prefill_prep_kernel<bf16, 512>), grid, dim3(256), 0, s, a);
+  else if (dtype == 0 && head_dim == 256) hipLaunchKernelGGL((prefill_prep_kernel<bf16, 256>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && head_dim == 512) hipLaunchKernelGGL((prefill_prep_kernel<float, 512>), grid, dim3(256), 0, s, a);
+  else if (dtype == 1 && head_dim == 256) hipLaunchKernelGGL((prefill_prep_kernel<float, 256>), grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const AppendArgs& a, int dtype, int head_dim, int batch, hipStream_t s) {
+  const dim3 grid(a.n_kv_heads, batch);
+  if (dtype == 0 && head_dim == 512) hipLaunchKernelGGL((kv_append_kernel<bf16, 512>), grid, dim3(64), 0, s, a);
+  else if (dtype == 0 && head_dim == 256) hipLaunchKernelGGL((kv_append_kernel<bf16, 256>), grid, dim3(64), 0, s, a);
+  else if (dtype == 1 && head_dim == 512) hipLaunchKernelGGL((kv_append_kernel<float, 512>), grid, dim3(64), 0, s, a);
+  else if (dtype == 1 && head_dim == 256) hipLaunchKernelGGL((kv_append_kernel<float, 256>), grid, dim3(64), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace ga

@@ -1,0 +1,186 @@
+/*
+ * gemma_attn.h -- C ABI of the MI355X (gfx950) attention block of a
+ * Gemma-4-style decoder: local sliding-window GQA layers and global K=V GQA
+ * layers with QKNorm and (p-)RoPE.
+ *
+ * Source of the method (all pages are about the "Gemma 4 Technical Report"):
+ *   - QKNorm (per-head RMSNorm of q and k): "Gemma 4 Technical Report" notes,
+ *     §2 Model Architecture; "Gemma 4 技术报告摘要", table "1. 预训练 Recipe".
+ *   - RoPE base 10k on local layers, p-RoPE p = 0.25 base 1M on global layers:
+ *     "Gemma 4 Technical Report" notes, §2 "Long-context efficiency";
+ *     "Gemma 4多模态大模型架构详解", section "p-RoPE（低频剪枝旋转位置编码）".
+ *   - keys reused as values on global layers: same notes §2; "Gemma 4多模态大模型
+ *     架构详解", section "K=V".
+ *   - GQA 2:1 local, 8:1 global, head dim 256 -> 512: "Gemma 4多模态大模型架构详解",
+ *     section "分组查询注意力"; "Gemma 4 架構與多模態拆解" talk notes, chapter
+ *     "Grouped query attention".
+ *   - sliding window (512 / 1024) and full causal attention: "Gemma 4多模态大模型
+ *     架构详解", section "交错层（局部与全局注意力）".
+ *
+ * Conventions fixed here (the pages leave them open):
+ *   - rotary pairs are adjacent dims (2i, 2i+1); pair i < n_rot = p*d/2 turns
+ *     counter-clockwise by pos * theta^(-2i/d); pairs >= n_rot are untouched;
+ *   - positions are 0-based; QKNorm is x / sqrt(mean(x^2) + eps) * gain;
+ *   - query head h reads KV head h / (n_q_heads / n_kv_heads);
+ *   - a window W keeps keys j with i - W < j <= i;
+ *   - K=V layers: the cache is ONE tensor of normalised, UNROTATED keys, slot j
+ *     = position j; p-RoPE is applied on the fly when scores are formed and the
+ *     unrotated tensor is the value;
+ *   - layers with a separate V: the K cache holds normalised and ROTATED keys and
+ *     the V cache the raw values; windowed layers keep a ring of W slots
+ *     (slot = position mod W).
+ *
+ * Ownership and execution:
+ *   - every pointer argument is caller-owned DEVICE memory except `layer`
+ *     (host).  Tensors are dense, row-major, in the layer's dtype unless stated.
+ *   - the library never allocates or frees device memory, never synchronises,
+ *     and keeps no pointer past a call.  Work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the null stream) and runs asynchronously.
+ *   - all argument validation happens on the host before any launch; a failed
+ *     validation launches nothing.  Device-resident values (positions, lengths)
+ *     are range-checked by the kernels, which then skip the write or write NaN
+ *     as documented per call.
+ *   - on any status other than GA_OK, gemma_attn_last_error() returns a message
+ *     for the calling thread.
+ *
+ * Supported on the GPU: head_dim 256 or 512; n_q_heads / n_kv_heads in
+ * {1, 2, 4, 8}; n_rot = rope_fraction * head_dim / 2 a whole multiple of 4 (any
+ * for separate-V layers, exactly 64 for K=V layers, e.g. d = 512 with
+ * p = 0.25); K=V only with window 0.  Other shapes return GA_EUNSUPPORTED.
+ */
+#ifndef GEMMA_ATTN_H
+#define GEMMA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GA_BF16 = 0, GA_F32 = 1 } ga_dtype;
+
+typedef enum {
+  GA_OK = 0,
+  GA_EINVAL = 1,        /* bad argument (null pointer, shape, size)         */
+  GA_EUNSUPPORTED = 2,  /* valid, but no kernel is built for this shape     */
+  GA_EWORKSPACE = 3,    /* workspace smaller than *_workspace_size() says   */
+  GA_EHIP = 4           /* a HIP launch failed; message holds the HIP error */
+} ga_status;
+
+/* One attention layer.  window = 0 is a global (full causal) layer. */
+typedef struct {
+  int32_t n_q_heads;      /* Hq                                               */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0                               */
+  int32_t head_dim;       /* d                                                */
+  int32_t window;         /* 0 = full causal; W > 0 = keys i-W < j <= i       */
+  int32_t kv_shared;      /* 1 = keys are the values (one cache tensor)       */
+  float rope_theta;       /* 1e4 on local layers, 1e6 on global layers        */
+  float rope_fraction;    /* p: 1.0 local, 0.25 global                        */
+  float norm_eps;         /* QKNorm epsilon, > 0 (1e-6)                       */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(d)                           */
+  int32_t dtype;          /* ga_dtype of every tensor; accumulation is fp32   */
+} ga_layer;
+
+/* Bytes of scratch gemma_attn_prefill needs for this batch and length. */
+size_t gemma_attn_prefill_workspace_size(const ga_layer* layer, int32_t batch,
+                                         int32_t seq_len);
+
+/*
+ * Prefill: causal attention over a whole prompt of seq_len tokens per sequence,
+ * and the cache fill.  Implements the attention of each layer type as stated
+ * above: QKNorm on q and k, (p-)RoPE at positions 0..S-1, GQA softmax attention
+ * with V = normalised unrotated K on K=V layers and V = v otherwise.
+ *
+ *   q       [B, S, Hq, d]   raw (post-projection, pre-norm, unrotated)
+ *   k       [B, S, Hkv, d]  raw
+ *   v       [B, S, Hkv, d]  raw; must be NULL when kv_shared = 1
+ *   q_gain, k_gain [d]      QKNorm gains
+ *   k_cache [B, Hkv, cache_cap, d] or NULL (no cache write).
+ *           K=V: slots 0..S-1 receive the normalised unrotated keys; needs
+ *           cache_cap >= S.  Windowed: ring of cache_cap == W slots receiving
+ *           the normalised rotated keys of positions max(0, S-W)..S-1.
+ *   v_cache like k_cache; windowed separate-V layers only (else NULL); gets v.
+ *   out     [B, S, Hq, d]
+ *   workspace  >= gemma_attn_prefill_workspace_size() bytes, 256-byte aligned.
+ * Errors: GA_EINVAL / GA_EUNSUPPORTED / GA_EWORKSPACE before any launch,
+ * GA_EHIP if a launch fails.  seq_len = 0 or batch = 0 is a no-op (GA_OK).
+ */
+ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_len,
+                             const void* q, const void* k, const void* v,
+                             const void* q_gain, const void* k_gain,
+                             void* k_cache, void* v_cache, int32_t cache_cap,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * Append one new token per sequence to the caches (decode step, before
+ * gemma_attn_decode).  The stored form follows the cache conventions above.
+ *
+ *   k_new   [B, Hkv, d] raw key of the new token;  v_new [B, Hkv, d] raw value
+ *           (NULL when kv_shared = 1)
+ *   k_gain  [d]
+ *   positions  device int32 [B]: position of the new token of each sequence.
+ *           K=V: slot = position; a position outside [0, cache_cap) writes
+ *           nothing.  Windowed: slot = position mod W; a negative position
+ *           writes nothing.
+ *   k_cache, v_cache, cache_cap as for gemma_attn_prefill.
+ */
+ga_status kv_append(const ga_layer* layer, int32_t batch,
+                    const void* k_new, const void* v_new, const void* k_gain,
+                    const int32_t* positions, void* k_cache, void* v_cache,
+                    int32_t cache_cap, void* stream);
+
+/* Bytes of scratch gemma_attn_decode needs (split-K partial results). */
+size_t gemma_attn_decode_workspace_size(const ga_layer* layer, int32_t batch,
+                                        int32_t max_seq_len);
+
+/*
+ * Decode: one query token per sequence against its cache (split-K over the
+ * cached positions, then a log-sum-exp merge of the partial results).
+ *
+ *   q        [B, Hq, d] raw query of the new token, at position seq_lens[b]-1
+ *   q_gain   [d]
+ *   k_cache, v_cache, cache_cap: as written by prefill / kv_append (v_cache
+ *            NULL when kv_shared = 1)
+ *   seq_lens device int32 [B]: valid keys including the new token (L_b >= 1).
+ *            K=V layers read slots 0..L_b-1; windowed layers the min(L_b, W)
+ *            filled ring slots.
+ *   max_seq_len host bound on every seq_lens[b], sizes the launch.  A sequence
+ *            with L_b < 1, L_b > max_seq_len or (K=V) L_b > cache_cap gets a NaN
+ *            output row instead of reading out of bounds.
+ *   out      [B, Hq, d]
+ *   workspace >= gemma_attn_decode_workspace_size() bytes, 256-byte aligned.
+ */
+ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch,
+                            const void* q, const void* q_gain,
+                            const void* k_cache, const void* v_cache,
+                            int32_t cache_cap, const int32_t* seq_lens,
+                            int32_t max_seq_len, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement hooks (not part of the computation).  While enabled, every
+ * launch of the kernels below is bracketed by a pair of HIP events recorded
+ * on the caller's stream; gemma_attn_profile_read() waits for the recorded
+ * events and returns the summed elapsed milliseconds and the launch count of
+ * one kernel: 0 prefill attention, 1 prefill prep (RoPE table + key/value
+ * preparation), 2 decode split-K, 3 decode merge, 4 kv_append.  Returns 0, or
+ * -1 if a HIP event call failed.  gemma_attn_profile_reset() destroys the
+ * recorded events.  Host-side bookkeeping only; thread-safe.
+ */
+void gemma_attn_profile_enable(int on);
+int gemma_attn_profile_read(int kernel, double* total_ms, int* count);
+void gemma_attn_profile_reset(void);
+
+/* Message for the last non-OK status returned to the calling thread. */
+const char* gemma_attn_last_error(void);
+
+/* Library version string. */
+const char* gemma_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMA_ATTN_H */

@@ -141,10 +141,11 @@ def masked_softmax_attention(q_rot, q_pos, k_rot, values, k_pos, scale: float,
 # --- The layer ---------------------------------------------------------------
 
 def _check_shapes(layer: OracleLayer, q, k, v):
-    B, S, Hq, d = q.shape
-    if Hq != layer.n_q_heads or d != layer.head_dim:
+    B, S, Hkv, d = k.shape
+    Hq = q.shape[2]
+    if Hq != layer.n_q_heads or d != layer.head_dim or q.shape[0] != B or q.shape[3] != d:
         raise ValueError("q shape does not match the layer")
-    if k.shape != (B, S, layer.n_kv_heads, d):
+    if Hkv != layer.n_kv_heads:
         raise ValueError("k shape does not match the layer")
     if layer.kv_shared:
         if v is not None:
@@ -155,18 +156,23 @@ def _check_shapes(layer: OracleLayer, q, k, v):
 
 
 def prefill(layer: OracleLayer, q, k, v, g_q, g_k, rows=None,
-            row_block: int = 512) -> np.ndarray:
+            row_block: int = 512, q_at_rows: bool = False) -> np.ndarray:
     """Attention output for a whole prompt.
 
     q [B,S,Hq,d], k [B,S,Hkv,d] and v [B,S,Hkv,d] (None for K=V) are the raw
     post-projection tensors.  Returns out [B, len(rows), Hq, d] for the query
-    positions ``rows`` (all positions by default).  Rows are evaluated
-    ``row_block`` at a time; each row is its own softmax, so this is the
-    definition evaluated row by row.
+    positions ``rows`` (all positions by default).  With ``q_at_rows`` the
+    caller passes q only at those rows, q [B, len(rows), Hq, d].  Rows are
+    evaluated ``row_block`` at a time; each row is its own softmax, so this is
+    the definition evaluated row by row.
     """
     B, S, Hq, d = _check_shapes(layer, q, k, v)
     G = layer.group
     rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    if q_at_rows and q.shape[1] != rows.size:
+        raise ValueError("q_at_rows: q must hold exactly the requested rows")
+    if not q_at_rows and q.shape[1] != S:
+        raise ValueError("q and k must have the same length")
     positions = np.arange(S)
 
     k_hat = qk_norm(k, g_k, layer.norm_eps)                          # [B,S,Hkv,d]
@@ -177,7 +183,8 @@ def prefill(layer: OracleLayer, q, k, v, g_q, g_k, rows=None,
     out = np.empty((B, rows.size, Hq, d), dtype=np.float64)
     for start in range(0, rows.size, row_block):
         r = rows[start:start + row_block]
-        q_hat = qk_norm(q[:, r], g_q, layer.norm_eps)                # [B,r,Hq,d]
+        q_r = q[:, start:start + row_block] if q_at_rows else q[:, r]
+        q_hat = qk_norm(q_r, g_q, layer.norm_eps)                   # [B,r,Hq,d]
         q_rot = rotate(q_hat, r[None, :, None], layer.rope_theta,
                        layer.rope_fraction)
         lo = 0 if layer.window == 0 else max(0, int(r.min()) - layer.window + 1)
@@ -257,11 +264,12 @@ def decode_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
         rows = np.empty((layer.n_q_heads, layer.head_dim))
         if layer.kv_shared:
             kpos = np.arange(L)
-            for h in range(layer.n_q_heads):
-                keys = _f64(k_cache[b, h // G, :L])
+            for c in range(layer.n_kv_heads):
+                keys = _f64(k_cache[b, c, :L])
                 k_rot = rotate(keys, kpos, layer.rope_theta, layer.rope_fraction)
-                rows[h] = masked_softmax_attention(q_rot[h:h + 1], qpos, k_rot,
-                                                   keys, kpos, layer.scale, 0)[0]
+                for h in range(c * G, (c + 1) * G):
+                    rows[h] = masked_softmax_attention(q_rot[h:h + 1], qpos, k_rot,
+                                                       keys, kpos, layer.scale, 0)[0]
         else:
             n = min(L, layer.window)
             # Slot s holds the latest position congruent to s mod W; all of the

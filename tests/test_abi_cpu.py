@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from global_gqa_rope_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemma_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keywords = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in keywords})
+
+
+def test_header_declarations_are_exported(lib):
+    names = declared_functions()
+    assert {"gemma_attn_prefill", "gemma_attn_decode", "kv_append"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gemma_attn.h but not exported"
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version(lib):
+    assert lib.gemma_attn_version().startswith(b"gemma_attn")
+
+
+def L(hq=32, hkv=4, d=512, window=0, shared=1, theta=1e6, p=0.25, eps=1e-6, dtype=0):
+    return _lib.GaLayer(hq, hkv, d, window, shared, theta, p, eps, 0.0, dtype)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def prefill(lib, layer, B=1, S=16, v=None, k_cache=None, v_cache=None, cap=0, ws=FAKE, ws_bytes=1 << 40):
+    return lib.gemma_attn_prefill(ctypes.byref(layer), B, S, FAKE, FAKE, v, FAKE, FAKE, k_cache,
+                                  v_cache, cap, FAKE, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("layer,status,msg", [
+    (L(hkv=5), 1, "multiple"),
+    (L(d=0), 1, "positive"),
+    (L(d=513), 1, "even"),
+    (L(p=0.3), 1, "whole number"),
+    (L(p=1.5), 1, "rope_fraction"),
+    (L(eps=0.0), 1, "norm_eps"),
+    (L(theta=-1.0), 1, "rope_theta"),
+    (L(dtype=7), 1, "dtype"),
+    (L(d=128, p=1.0), 2, "head_dim"),
+    (L(hq=48, hkv=3), 2, "1, 2, 4, 8"),
+    (L(window=64), 2, "window 0"),
+    (L(p=0.5), 2, "64 pairs"),
+])
+def test_layer_validation(lib, layer, status, msg):
+    assert prefill(lib, layer) == status
+    assert msg in lib.gemma_attn_last_error().decode()
+
+
+def test_prefill_argument_validation(lib):
+    g = L()
+    assert prefill(lib, g, v=FAKE) == 1                      # K=V takes no v
+    loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
+    assert prefill(lib, loc, v=None) == 1                    # local needs v
+    assert prefill(lib, loc, v=FAKE, k_cache=FAKE, v_cache=FAKE, cap=512) == 1   # ring = W
+    assert "must equal window" in lib.gemma_attn_last_error().decode()
+    assert prefill(lib, g, k_cache=FAKE, cap=8, S=16) == 1   # cache too small
+    assert prefill(lib, g, k_cache=FAKE, v_cache=FAKE, cap=64) == 1
+    assert prefill(lib, g, ws=None, ws_bytes=0) == 3
+    need = lib.gemma_attn_prefill_workspace_size(ctypes.byref(g), 1, 16)
+    assert need > 0
+    assert prefill(lib, g, ws_bytes=need - 1) == 3
+    assert prefill(lib, g, ws=ctypes.c_void_p(0x1001)) == 1  # alignment
+    assert prefill(lib, g, B=-1) == 1
+    assert prefill(lib, g, B=0) == 0 and prefill(lib, g, S=0) == 0   # no-ops, no launch
+
+
+def test_decode_and_append_validation(lib):
+    g = L()
+    dec = lambda **kw: lib.gemma_attn_decode(
+        ctypes.byref(kw.get("layer", g)), kw.get("B", 2), FAKE, FAKE, FAKE, kw.get("v", None),
+        kw.get("cap", 4096), FAKE, kw.get("max_len", 4096), FAKE, kw.get("ws", FAKE),
+        kw.get("ws_bytes", 1 << 40), None)
+    assert dec(v=FAKE) == 1
+    assert dec(max_len=0) == 1
+    assert dec(cap=0) == 1
+    assert dec(ws=None, ws_bytes=0) == 3
+    assert dec(B=0) == 0
+    need = lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 4096)
+    assert need >= 2 * 4 * 4 * 8 * 514 * 4
+    # one chunk needs no partials, so no workspace
+    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 1000) == 0
+    app = lambda **kw: lib.kv_append(ctypes.byref(kw.get("layer", g)), 2, FAKE, kw.get("v", None),
+                                     FAKE, kw.get("pos", FAKE), FAKE, kw.get("vc", None),
+                                     kw.get("cap", 4096), None)
+    assert app(v=FAKE) == 1
+    assert app(pos=None) == 1
+    loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
+    assert app(layer=loc, v=FAKE, vc=None, cap=1024) == 1
+
+
+def test_workspace_sizes_follow_the_layout(lib):
+    g = L()
+    # table (S_pad * 64 pairs * 8 B) + two [B,Hkv,S_pad,512] bf16 tile sets
+    s_pad = 32768
+    want = s_pad * 64 * 8 + 2 * (1 * 4 * s_pad * 512 * 2)
+    assert lib.gemma_attn_prefill_workspace_size(ctypes.byref(g), 1, 32768) == want
+    loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
+    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(loc), 32, 65537) == 0   # W = one chunk
