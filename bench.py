@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
     return ap.parse_args()
 
 
@@ -156,6 +158,13 @@ def main():
     from global_gqa_rope_amd import api
     from global_gqa_rope_amd import workloads as W
 
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     pre = bench_prefill(args, torch, api, W)
     tflops = pre["flops"] / pre["sec"] / 1e12
     attn_tflops = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12

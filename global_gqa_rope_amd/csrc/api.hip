@@ -316,6 +316,9 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
   if (batch < 0) return fail(GA_EINVAL, "batch must be >= 0");
   if (batch == 0) return GA_OK;
   if (max_seq_len < 1) return fail(GA_EINVAL, "max_seq_len must be >= 1");
+  if (decode_chunks(layer, max_seq_len) > 1024)
+    return fail(GA_EUNSUPPORTED, "max_seq_len %d: decode supports up to %d cached positions", max_seq_len,
+                1024 * ga::kDecodeChunk);
   if (!q || !q_gain || !seq_lens || !out) return fail(GA_EINVAL, "q, q_gain, seq_lens and out must be non-NULL");
   st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
   if (st != GA_OK) return st;

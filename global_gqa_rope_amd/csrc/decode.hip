@@ -333,29 +333,52 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Log-sum-exp merge of the chunk partials of one (sequence, KV head).
+// Log-sum-exp merge of the chunk partials of one (sequence, query head): the
+// chunk weights exp2(m_c - M) are computed once into LDS, then each thread
+// accumulates whole head dims across chunks (consecutive threads, consecutive
+// dims).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  const int kvh = blockIdx.x, b = blockIdx.y;
+  __shared__ float wgt[1024];
+  __shared__ float red[256];
+  const int h = blockIdx.x % G, kvh = blockIdx.x / G, b = blockIdx.y;
   const int nkeys = decode_keys(a, b, false);
   if (nkeys < 0) return;
   const int n_chunks = (nkeys + kDecodeChunk - 1) / kDecodeChunk;
   if (n_chunks <= 1) return;
   const int64_t head = static_cast<int64_t>(b) * a.n_kv_heads + kvh;
-  const float* part = a.partials + head * a.n_chunks * G * (D + 2);
-  T* __restrict__ out = static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G) * D;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D, d = i % D;
-    float M = -INFINITY;
-    for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, part[(c * G + h) * (D + 2)]);
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float* pc = part + (c * G + h) * (D + 2);
-      const float e = __builtin_amdgcn_exp2f(pc[0] - M);
-      L += e * pc[1];
-      O += e * pc[2 + d];
-    }
-    out[h * D + d] = from_f32<T>(O / L);
+  const float* part = a.partials + head * a.n_chunks * G * (D + 2) + h * (D + 2);
+  constexpr int kStride = G * (D + 2);          // floats between chunks
+  const int t = threadIdx.x;
+
+  float mx = -INFINITY;
+  for (int c = t; c < n_chunks; c += 256) mx = fmaxf(mx, part[c * kStride]);
+  red[t] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) red[t] = fmaxf(red[t], red[t + s]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float lsum = 0.f;
+  for (int c = t; c < n_chunks; c += 256) {
+    const float w = __builtin_amdgcn_exp2f(part[c * kStride] - M);
+    wgt[c] = w;
+    lsum += w * part[c * kStride + 1];
+  }
+  red[t] = lsum;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) red[t] += red[t + s];
+    __syncthreads();
+  }
+  const float inv = 1.0f / red[0];
+  T* __restrict__ out = static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G + h) * D;
+  for (int d = t; d < D; d += 256) {
+    float o = 0.f;
+    for (int c = 0; c < n_chunks; ++c) o += wgt[c] * part[c * kStride + 2 + d];
+    out[d] = from_f32<T>(o * inv);
   }
 }
 
@@ -369,7 +392,7 @@ static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t s, Laun
   if (timer) timer(s, 2, false);
   if (e != hipSuccess || a.n_chunks <= 1) return e;
   if (timer) timer(s, 3, true);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(a.n_kv_heads, batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(a.n_kv_heads * G, batch), dim3(256), 0, s, a);
   e = hipGetLastError();
   if (timer) timer(s, 3, false);
   return e;
