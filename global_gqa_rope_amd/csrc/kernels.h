@@ -11,23 +11,26 @@ namespace ga {
 constexpr int kPrepTile = 32;      // key positions per prefill tile (prep and attention)
 constexpr int kDecodeChunk = 1024; // cached positions per decode workgroup
 
-// Prefill tiles in MFMA operand order.  A tile of kPrepTile keys is a sequence
-// of fragments; fragment f holds, for each of the 64 lanes of a wave, the 8
-// elements that lane feeds to one 32x32 MFMA.  Inside a fragment, element j of
-// lane l sits at byte ((j * sizeof(T)) / 16) * 1024 + l * 16 + (j * sizeof(T)) % 16,
-// so every operand read is 1 KiB of consecutive LDS bytes (lane order).
-//   key tile, fragment u (u < D/16):   lane l, element j = K~[key l%32][16u + 8(l/32) + j]
-//   value tile, fragment 2t+s (t < D/32, s < 2):
-//     lane l, element j = V[key perm(16s + 8(l/32) + j)][32t + l%32]
-//   perm swaps bits 2 and 3 of the key index (the order in which the score
-//   accumulator lanes hold keys).
+// Prefill tiles in MFMA operand order.  A tile of kPrepTile = 32 keys is a
+// sequence of 1 KiB fragments; fragment f holds, for each of the 64 lanes of a
+// wave, the 8 elements that lane feeds one 16x16x32 MFMA.  Inside a fragment,
+// element j of lane l sits at byte ((j * sizeof(T)) / 16) * 1024 + l * 16 +
+// (j * sizeof(T)) % 16, so every operand read is 1 KiB of consecutive LDS bytes.
+// With g = l / 16 (the lane's reduction group):
+//   key tile, fragment 2u + b (u < D/32, b < 2):
+//     lane l, element j = K~[key 16b + l%16][32u + 8g + j]
+//   value tile, fragment t (t < D/16):
+//     lane l, element j = V[key tile_key(g, j)][16t + l%16]
+//   tile_key(g, j) = 4g + j for j < 4 and 16 + 4g + (j - 4) for j >= 4: the
+//   keys a 16x16 score accumulator lane holds for its column, so P goes from
+//   the score registers into the PV operand unchanged.
 template <typename T>
 __host__ __device__ constexpr int frag_bytes() { return 64 * 8 * int(sizeof(T)); }
 template <typename T>
 __host__ __device__ inline int frag_elem_off(int lane, int j) {
   return (j * int(sizeof(T)) / 16) * 1024 + lane * 16 + (j * int(sizeof(T))) % 16;
 }
-__host__ __device__ constexpr int key_perm(int q) { return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1); }
+__host__ __device__ constexpr int tile_key(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
 
 struct PrepArgs {
   const void* k;

@@ -104,16 +104,17 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
     }
   }
 
-  // Rotated keys into the operand-ordered key tile (padded rows zero).  Chunk c
-  // of row r is fragment c/2, lane r + 32 (c & 1).
+  // Rotated keys into the operand-ordered key tile (padded rows zero).  The
+  // 8-element chunk c of key r is fragment 2 (c / 4) + r / 16, lane
+  // r % 16 + 16 (c % 4).
   const int64_t tile_base = (head_base * (a.seq_pad / kPrepTile) + tile) * (kPrepTile * D);
   {
     char* kt = reinterpret_cast<char*>(static_cast<T*>(a.ws_k) + tile_base);
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
       const int c = i * 8 + c8;
-      char* frag = kt + (c >> 1) * frag_bytes<T>();
-      const int ln = r + 32 * (c & 1);
+      char* frag = kt + (2 * (c >> 2) + (r >> 4)) * frag_bytes<T>();
+      const int ln = (r & 15) + 16 * (c & 3);
 #pragma unroll
       for (int j = 0; j < 8; ++j) *reinterpret_cast<T*>(frag + frag_elem_off<T>(ln, j)) = from_f32<T>(x[i][j]);
     }
@@ -150,21 +151,18 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  // Values into the operand-ordered value tile: column d of the staged tile
-  // goes to fragments 2 (d / 32) + s, lanes d % 32 + 32 g.
+  // Values into the operand-ordered value tile: head dim d goes to fragment
+  // d / 16, lanes d % 16 + 16 g, element j holding key tile_key(g, j).
   {
     char* vt = reinterpret_cast<char*>(static_cast<T*>(a.ws_vt) + tile_base);
     for (int d = t; d < D; d += 256) {
+      char* frag = vt + (d >> 4) * frag_bytes<T>();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int g = 0; g < 4; ++g) {
+        const int ln = (d & 15) + 16 * g;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          char* frag = vt + (2 * (d / 32) + s) * frag_bytes<T>();
-          const int ln = (d & 31) + 32 * g;
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<T*>(frag + frag_elem_off<T>(ln, j)) = vtile[key_perm(16 * s + 8 * g + j)][d];
-        }
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<T*>(frag + frag_elem_off<T>(ln, j)) = vtile[tile_key(g, j)][d];
       }
     }
   }
