@@ -320,6 +320,8 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
     return fail(GA_EUNSUPPORTED, "max_seq_len %d: decode supports up to %d cached positions", max_seq_len,
                 1024 * ga::kDecodeChunk);
   if (!q || !q_gain || !seq_lens || !out) return fail(GA_EINVAL, "q, q_gain, seq_lens and out must be non-NULL");
+  if (layer->dtype == GA_F32 && layer->head_dim == 512 && !layer->kv_shared)
+    return fail(GA_EUNSUPPORTED, "fp32 decode with head_dim 512 and a separate V cache is not built");
   st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
   if (st != GA_OK) return st;
   const size_t need = decode_bytes(layer, dv, batch, max_seq_len);
