@@ -23,6 +23,10 @@ LIB_NAME = "libgemma_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "prep.hip", "prefill.hip", "decode.hip"]
 ARCH = "gfx950"
+# Per-source device flags.  The decode kernel keeps its 128 fp32 output
+# accumulators in VGPRs and rescales them with VALU ops: MFMAs in VGPR form
+# avoid copying them between the two register files every tile.
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -45,7 +49,7 @@ def build(jobs: int = 8, verbose: bool = False, extra: list[str] | None = None) 
     try:
         def compile_one(src: str) -> str:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [cc, *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *common_flags(), *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             res = subprocess.run(cmd, capture_output=True, text=True)

@@ -324,6 +324,8 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
     return fail(GA_EUNSUPPORTED, "fp32 decode with head_dim 512 and a separate V cache is not built");
   st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
   if (st != GA_OK) return st;
+  if (static_cast<int64_t>(cache_cap) * layer->head_dim * dv.elem > INT32_MAX)
+    return fail(GA_EUNSUPPORTED, "cache_cap %d: one head's cache must stay under 2 GiB for decode", cache_cap);
   const size_t need = decode_bytes(layer, dv, batch, max_seq_len);
   st = check_workspace(workspace, workspace_bytes, need);
   if (st != GA_OK) return st;

@@ -2,25 +2,35 @@
 //
 // Work item = (chunk of kDecodeChunk cached positions, KV head, sequence).  Each
 // wave of the workgroup streams its share of the chunk in tiles of 16 keys:
-//   global -> LDS by direct-to-LDS copies, two tiles per wave, the next tile
-//   already in flight while the current one is computed (no register staging);
+//   global -> LDS by buffer loads that write LDS directly, two tiles per wave,
+//   the next tile in flight while the current one is computed;
 //   K=V layers: pairs 0..63 of every key are rotated on the fly as they are
 //   loaded into the QK^T operand (p-RoPE of the "Gemma 4多模态大模型架构详解"
 //   section "p-RoPE（低频剪枝旋转位置编码）"); the raw rows in LDS are the values
 //   ("K=V" section of the same page);
-//   S^T[key][head] = K~ Q~^T   (16x16x32 MFMA, the G heads padded to 16 columns)
-//   online softmax per head (wave shuffles, exp2 domain)
+//   S^T[key][head] = K~ Q~^T   (16x16x32 MFMA, the G heads padded to 16 columns;
+//                               the query operand is read from LDS, where the
+//                               workgroup wrote it once in operand order)
+//   online softmax per head (exp2 domain, lazy rescale)
 //   O^T[d][head] += V^T P^T     (16x16x16 MFMA; V^T by LDS transpose reads, P
 //                               straight from the S^T registers)
 // The waves then merge through LDS into one partial (max, sum, o) per item, or
 // the final row when the item is the sequence's only chunk; a second kernel
 // merges the partials of longer sequences by log-sum-exp.
+//
+// All LDS addressing inside the loop is one XOR per read: tiles sit at
+// multiples of their size and rows at multiples of the row size, and a
+// fragment's 16-byte chunk index splits into a lane part and a per-step part
+// with disjoint bits, so the row swizzle (chunk c of row r at c ^ (r & 15))
+// turns into lane_base ^ (step part << 4).
 #include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace ga {
+
+constexpr int kLdsLimit = 160 * 1024;
 
 template <typename T, int D, int G, bool SHARED>
 struct DecodeCfg {
@@ -29,21 +39,56 @@ struct DecodeCfg {
   static constexpr int kRot = SHARED ? 64 : 0;        // pairs rotated on the fly
   static constexpr int kRotSteps = 2 * kRot / 32;     // QK^T steps that cover rotated dims
   static constexpr int kRowBytes = D * kSz;           // one key row
-  static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kKBytes = KT * kRowBytes;      // key tile (the values too for K=V)
   static constexpr int kTileBytes = SHARED ? kKBytes : 2 * kKBytes;   // + value tile
   static constexpr int kBufs = 2;                     // tiles in LDS per wave
-  static constexpr int kWaves = (4 * kBufs * kTileBytes <= 128 * 1024) ? 4 : 2;
-  static constexpr int kPerWave = kDecodeChunk / kWaves;
   static constexpr int kQSteps = D / 32;              // QK^T reduction steps
   static constexpr int kDBlocks = D / 16;             // PV output blocks of 16 dims
+  static constexpr int kFragBytes = 64 * 8 * kSz;     // one query operand fragment
+  static constexpr int kQBytes = kQSteps * kFragBytes;
+  static constexpr int kFineBytes = 16 * kRot * 8;    // cos/sin(j w_i), j < 16, i < kRot
+  static constexpr int kCoarseBytes = kRot * 8;       // per wave: cos/sin(key0 w_i)
+  static constexpr int kPerWaveBytes = kBufs * kTileBytes + kCoarseBytes;
+  static constexpr int kCommonBytes = kQBytes + kFineBytes;
+  static constexpr int kWaves = (4 * kPerWaveBytes + kCommonBytes <= kLdsLimit)   ? 4
+                                : (2 * kPerWaveBytes + kCommonBytes <= kLdsLimit) ? 2
+                                                                                  : 1;
+  static constexpr int kPerWave = kDecodeChunk / kWaves;
   static constexpr int kDmaPerTile = kTileBytes / 1024;
-  static constexpr int kWaveLds = kBufs * kTileBytes + 64 * 8;   // tiles + coarse angles
-  static constexpr int kCombineBytes = kWaves * (G * D + 32) * 4;
-  static constexpr int kLdsBytes = (kWaves * kWaveLds > kCombineBytes) ? kWaves * kWaveLds : kCombineBytes;
-  static_assert(kChunksPerRow >= 16, "row swizzle needs 16 chunks per row");
+  static constexpr int kKDma = kKBytes / 1024;
+  // LDS map: [wave][buf] tiles | [wave] coarse angles | query operand | fine angles
+  static constexpr int kCoarseOff = kWaves * kBufs * kTileBytes;
+  static constexpr int kQOff = kCoarseOff + kWaves * kCoarseBytes;
+  static constexpr int kFineOff = kQOff + kQBytes;
+  static constexpr int kLdsBytes = kFineOff + kFineBytes;
+  static constexpr int kCombineBytes = kWaves * (G * D + 32) * 4;   // reuses the tiles
+  static_assert(kLdsBytes <= kLdsLimit, "LDS budget");
+  static_assert(kCombineBytes <= kCoarseOff, "wave combine area must fit in the tile area");
+  static_assert(kRowBytes / 16 >= 16, "row swizzle needs 16 chunks per row");
   static_assert(kTileBytes % 1024 == 0 && kDmaPerTile < 64, "tile copy");
 };
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
+}
+template <typename V>
+__device__ __forceinline__ V lds_ld(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) V*)(static_cast<uintptr_t>(addr));
+}
+template <typename V>
+__device__ __forceinline__ void lds_st(uint32_t addr, V v) {
+  *(__attribute__((address_space(3))) V*)(static_cast<uintptr_t>(addr)) = v;
+}
+
+// Raw buffer over `bytes` bytes: loads past the end return zeros instead of
+// touching memory (dword 3: 32-bit data format, as untyped buffer loads need).
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
 
 // Orders this wave's LDS accesses (compiler and hardware) around a tile reuse.
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -64,70 +109,150 @@ __device__ __forceinline__ int decode_keys(const DecodeArgs& a, int b) {
 __device__ __forceinline__ int row_chunk(int r, int c) { return c ^ (r & 15); }
 
 // Copy one tile (16 key rows, plus 16 value rows for separate-V layers) from
-// global memory straight into LDS.  Each instruction moves 1 KiB: the lane
-// fetches the global chunk that the swizzle places at its LDS slot.  Rows
-// past the sequence read its last row (their scores are masked).
-template <typename T, int D, int G, bool SHARED>
-__device__ __forceinline__ void issue_tile(char* dst, const char* kbase, const char* vbase, int key0,
-                                           int nkeys, int lane) {
-  using C = DecodeCfg<T, D, G, SHARED>;
+// the cache straight into LDS at `dst`.  Each instruction moves 1 KiB: lane l
+// writes LDS slot dst + 16 l and fetches the cache chunk that the swizzle
+// places there.  Rows past the sequence read its last row (their scores are
+// masked); the buffer's range check backs this up.
+template <typename C>
+__device__ __forceinline__ void issue_tile(uint32_t dst, BufRsrc rk, BufRsrc rv, int key0, int nkeys, int lane) {
 #pragma unroll
   for (int i = 0; i < C::kDmaPerTile; ++i) {
-    const int off = (i % (C::kKBytes / 1024)) * 1024 + lane * 16;
-    const int r = off / C::kRowBytes;
-    const int pc = (off % C::kRowBytes) >> 4;
-    const int key = min(key0 + r, nkeys - 1);
-    const char* base = (SHARED || i < C::kKBytes / 1024) ? kbase : vbase;
-    const char* src = base + static_cast<int64_t>(key) * C::kRowBytes + (row_chunk(r, pc) << 4);
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+    const int ik = i % C::kKDma;                   // 1 KiB piece within the K (or V) tile
+    const BufRsrc& rs = (i < C::kKDma) ? rk : rv;
+    lds_char* slot = (lds_char*)(static_cast<uintptr_t>(dst + i * 1024));
+    if constexpr (C::kRowBytes >= 1024) {          // piece inside one row: the key is wave-uniform
+      constexpr int kPiecesPerRow = C::kRowBytes / 1024;
+      const int r = ik / kPiecesPerRow;
+      const int s = (ik % kPiecesPerRow) * 64 + lane;
+      const int key = min(key0 + r, nkeys - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, slot, 16, row_chunk(r, s) << 4, key * C::kRowBytes, 0, 0);
+    } else {                                       // several rows per piece
+      constexpr int kChunksPerRow = C::kRowBytes / 16;
+      const int r = ik * (1024 / C::kRowBytes) + lane / kChunksPerRow;
+      const int s = lane % kChunksPerRow;
+      const int key = min(key0 + r, nkeys - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, slot, 16, key * C::kRowBytes + (row_chunk(r, s) << 4), 0, 0, 0);
+    }
   }
 }
 
-// The 8 elements of key row r starting at logical chunk c (QK^T A operand):
-// one chunk for bf16, two for fp32.
-__device__ __forceinline__ void row_frag(Frag8<bf16>& f, const char* row, int r, int c) {
-  f.v = *reinterpret_cast<const bf16x8*>(row + (row_chunk(r, c) << 4));
+// QK^T A operand: the 8 elements of the lane's key row at dims 32u + 8kg .. +7.
+// `a` = lane base (row hcol, lane chunk part); the step part is XORed in.
+template <typename C>
+__device__ __forceinline__ void key_frag(Frag8<bf16>& f, uint32_t a, int u) {
+  f.v = lds_ld<bf16x8>(a ^ ((4 * u) << 4));
 }
-__device__ __forceinline__ void row_frag(Frag8<float>& f, const char* row, int r, int c) {
-  const f32x4 lo = *reinterpret_cast<const f32x4*>(row + (row_chunk(r, c) << 4));
-  const f32x4 hi = *reinterpret_cast<const f32x4*>(row + (row_chunk(r, c + 1) << 4));
+template <typename C>
+__device__ __forceinline__ void key_frag(Frag8<float>& f, uint32_t a, int u) {
+  const f32x4 lo = lds_ld<f32x4>(a ^ ((8 * u) << 4));
+  const f32x4 hi = lds_ld<f32x4>(a ^ ((8 * u) << 4) ^ 16);
   f.v[0] = lo[0]; f.v[1] = lo[1]; f.v[2] = lo[2]; f.v[3] = lo[3];
   f.v[4] = hi[0]; f.v[5] = hi[1]; f.v[6] = hi[2]; f.v[7] = hi[3];
 }
 
-// V^T fragment for a 16x16x16 MFMA: lane l needs V[key 4(l/16) + j][d0 + l%16],
+// PV A operand V^T for dims 16t .. +15: lane l needs V[key 4(l/16) + j][16t + l%16],
 // j = 0..3.  bf16: one transpose read (within each 16-lane group, lane i gets
-// element i%4 of the 8-byte pieces addressed by lanes i/4 + 4j); each lane
-// addresses key 4(l/16) + (l%16)/4, dims d0 + 4 (l%4) .. +3.  fp32: four reads.
-template <int kRowBytes>
-__device__ __forceinline__ void vt_frag(Frag4<bf16>& f, const char* vt, int d0, int lane) {
-  const int r = 4 * (lane >> 4) + ((lane & 15) >> 2);
-  const int byte = (d0 + 4 * (lane & 3)) * 2;
-  const char* p = vt + r * kRowBytes + (row_chunk(r, byte >> 4) << 4) + (byte & 15);
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+// element i%4 of the 8-byte pieces addressed by lanes i/4 + 4j); lane l
+// addresses key 4(l/16) + (l%16)/4, dims 16t + 4(l%4) .. +3, whose chunk is
+// 2t + (l%4)/2.  fp32: four plain reads (rows 4(l/16) + j, dim 16t + l%16).
+template <typename C>
+__device__ __forceinline__ void value_frag(Frag4<bf16>& f, uint32_t a, int t) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(static_cast<uintptr_t>(a ^ ((2 * t) << 4))));
   f.v = __builtin_bit_cast(bf16x4, v);
 }
-template <int kRowBytes>
-__device__ __forceinline__ void vt_frag(Frag4<float>& f, const char* vt, int d0, int lane) {
-  const int d = d0 + (lane & 15);
-  const int byte = d * 4;
+template <typename C>
+__device__ __forceinline__ void value_frag(Frag4<float>& f, uint32_t vtile, int t) {
+  const int lane = threadIdx.x & 63;
+  const int cvar = (lane & 15) >> 2;              // chunk of dim 16t + l%16 is 4t + cvar
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 4 * (lane >> 4) + j;
-    f.v[j] = *reinterpret_cast<const float*>(vt + r * kRowBytes + (row_chunk(r, byte >> 4) << 4) + (byte & 15));
+    const uint32_t at = vtile + r * C::kRowBytes + ((cvar ^ r) << 4) + 4 * (lane & 3);
+    f.v[j] = lds_ld<float>(at ^ ((4 * t) << 4));
   }
 }
 
+// Per-lane base addresses (tile buffer 0) of the two operand reads.
+template <typename C, typename T>
+__device__ __forceinline__ uint32_t key_lane_base(uint32_t tile, int lane) {
+  const int hcol = lane & 15, kg = lane >> 4;
+  const int cvar = kg * C::kSz / 2;               // lane part of chunk (32u + 8kg) * size / 16
+  return tile + hcol * C::kRowBytes + ((cvar ^ hcol) << 4);
+}
+template <typename C, typename T>
+__device__ __forceinline__ uint32_t value_lane_base(uint32_t vtile, int lane) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    const int r = 4 * (lane >> 4) + ((lane & 15) >> 2);
+    const int cvar = (lane & 3) >> 1;
+    return vtile + r * C::kRowBytes + ((cvar ^ r) << 4) + 8 * (lane & 1);
+  } else {
+    return vtile;                                 // the fp32 reads form their own lane addresses
+  }
+}
+
+// Query operand fragment u of this lane (written once per workgroup).
+__device__ __forceinline__ void load_qfrag(Frag8<bf16>& f, uint32_t a) { f.v = lds_ld<bf16x8>(a); }
+__device__ __forceinline__ void load_qfrag(Frag8<float>& f, uint32_t a) {
+  const f32x4 lo = lds_ld<f32x4>(a), hi = lds_ld<f32x4>(a + 16);
+  f.v[0] = lo[0]; f.v[1] = lo[1]; f.v[2] = lo[2]; f.v[3] = lo[3];
+  f.v[4] = hi[0]; f.v[5] = hi[1]; f.v[6] = hi[2]; f.v[7] = hi[3];
+}
+
+// One QK^T step's operands: key fragment, query fragment and, for the
+// rotated steps, the coarse and fine angle factors of the lane's 4 pairs.
+template <typename T>
+struct QkStep {
+  Frag8<T> kf, qf;
+  f32x2 cb[4], fj[4];
+};
+template <typename C, typename T>
+__device__ __forceinline__ void load_step(QkStep<T>& st, int u, uint32_t k_lane, uint32_t q_lane,
+                                          uint32_t coarse_lane, uint32_t fine_lane) {
+  key_frag<C>(st.kf, k_lane, u);
+  load_qfrag(st.qf, q_lane + u * C::kFragBytes);
+  if (u < C::kRotSteps) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      st.cb[p] = lds_ld<f32x2>(coarse_lane + (16 * u + p) * 8);
+      st.fj[p] = lds_ld<f32x2>(fine_lane + (16 * u + p) * 8);
+    }
+  }
+}
+// Rotate the 4 pairs of a key fragment by cos/sin = coarse (x) fine.
+template <typename T>
+__device__ __forceinline__ void rotate_step(QkStep<T>& st) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    f32x2 cs;
+    cs[0] = st.cb[p][0] * st.fj[p][0] - st.cb[p][1] * st.fj[p][1];
+    cs[1] = st.cb[p][1] * st.fj[p][0] + st.cb[p][0] * st.fj[p][1];
+    float x0 = to_f32(st.kf.v[2 * p]), x1 = to_f32(st.kf.v[2 * p + 1]);
+    rotate_pair(x0, x1, cs);
+    frag_set(st.kf, 2 * p, x0);
+    frag_set(st.kf, 2 * p + 1, x1);
+  }
+}
+
+// Max over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48),
+// with the gfx950 row-swap moves instead of LDS permutes.
+__device__ __forceinline__ float max_across_kg(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const unsigned v = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 template <typename T, int D, int G, bool SHARED>
-__global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, G, SHARED>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
-  __shared__ float q_s[G][D];          // normalised, rotated, pre-scaled queries
-  __shared__ f32x2 qcs[D / 2];         // (cos, sin) at the query position
-  __shared__ float rstd_s[G];
+  __shared__ __attribute__((aligned(4096))) char smem[C::kLdsBytes];
 
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
   constexpr int kThreads = C::kWaves * 64;
   const int nkeys = decode_keys(a, b);
   T* __restrict__ out = static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G) * D;
@@ -143,119 +268,130 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
 
   // ---- stream setup: start this wave's first two tile copies right away -----
   const int64_t head = static_cast<int64_t>(b) * a.n_kv_heads + kvh;
-  const char* kbase = static_cast<const char*>(a.k_cache) + head * a.cache_cap * static_cast<int64_t>(C::kRowBytes);
-  const char* vbase = SHARED ? kbase
-                             : static_cast<const char*>(a.v_cache) + head * a.cache_cap * static_cast<int64_t>(C::kRowBytes);
-  char* wlds = smem + wave * C::kWaveLds;
-  f32x2* coarse_s = reinterpret_cast<f32x2*>(wlds + C::kBufs * C::kTileBytes);
+  const uint32_t span = static_cast<uint32_t>(a.cache_cap) * C::kRowBytes;   // < 2^31 (checked on the host)
+  const BufRsrc rk = make_rsrc(static_cast<const char*>(a.k_cache) + head * span, span);
+  const BufRsrc rv = SHARED ? rk : make_rsrc(static_cast<const char*>(a.v_cache) + head * span, span);
+  const uint32_t smem0 = lds_addr(smem);
+  const uint32_t tiles = smem0 + wave * C::kBufs * C::kTileBytes;
   const int w0 = c0 + wave * C::kPerWave;
   const int w1 = min(w0 + C::kPerWave, nkeys);
   const int ntiles = w1 > w0 ? (w1 - w0 + C::KT - 1) / C::KT : 0;
-  if (ntiles > 0) issue_tile<T, D, G, SHARED>(wlds, kbase, vbase, w0, nkeys, lane);
-  if (ntiles > 1) issue_tile<T, D, G, SHARED>(wlds + C::kTileBytes, kbase, vbase, w0 + C::KT, nkeys, lane);
+  if (ntiles > 0) issue_tile<C>(tiles, rk, rv, w0, nkeys, lane);
+  if (ntiles > 1) issue_tile<C>(tiles + C::kTileBytes, rk, rv, w0 + C::KT, nkeys, lane);
 
-  // ---- query prep: QKNorm + rotation at qpos, into LDS --------------------------
+  // ---- query prep: QKNorm + rotation at qpos, written in operand order --------
+  // Operand fragment u, lane hcol + 16 kg, element j = q~[hcol][32u + 8kg + j]
+  // (heads >= G are zeros).  One wave per head: lane owns pairs lane + 64 m.
   {
+    constexpr int kPairsPerLane = D / 128;
     const T* __restrict__ q = static_cast<const T*>(a.q) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G) * D;
     const T* __restrict__ gq = static_cast<const T*>(a.q_gain);
-    for (int i = threadIdx.x; i < a.n_rot; i += kThreads)
-      qcs[i] = rope_cos_sin(static_cast<double>(qpos) * rope_omega(i, D, a.log2_theta));
-    for (int h = wave; h < G; h += C::kWaves) {
+    f32x2 qcs[kPairsPerLane];
+#pragma unroll
+    for (int m = 0; m < kPairsPerLane; ++m) {
+      const int pr = lane + 64 * m;
+      qcs[m] = pr < a.n_rot ? rope_cos_sin(static_cast<double>(qpos) * rope_omega(pr, D, a.log2_theta))
+                            : f32x2{1.f, 0.f};
+    }
+    for (int h = wave; h < 16; h += C::kWaves) {
+      float x[kPairsPerLane][2];
       float ss = 0.f;
-      for (int d = lane; d < D; d += 64) {
-        const float x = to_f32(q[h * D + d]);
-        ss += x * x;
+#pragma unroll
+      for (int m = 0; m < kPairsPerLane; ++m) {
+        const int pr = lane + 64 * m;
+        x[m][0] = h < G ? to_f32(q[h * D + 2 * pr]) : 0.f;
+        x[m][1] = h < G ? to_f32(q[h * D + 2 * pr + 1]) : 0.f;
+        ss += x[m][0] * x[m][0] + x[m][1] * x[m][1];
       }
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) ss += wave_xor(ss, m);
-      if (lane == 0) rstd_s[h] = 1.0f / sqrtf(ss / D + a.eps);
+      for (int s = 1; s < 64; s <<= 1) ss += wave_xor(ss, s);
+      const float rstd = 1.0f / sqrtf(ss / D + a.eps);
+#pragma unroll
+      for (int m = 0; m < kPairsPerLane; ++m) {
+        const int pr = lane + 64 * m;
+        float x0 = x[m][0] * rstd * to_f32(gq[2 * pr]);
+        float x1 = x[m][1] * rstd * to_f32(gq[2 * pr + 1]);
+        rotate_pair(x0, x1, qcs[m]);
+        const int u = pr / 16, kg = (pr % 16) / 4, j = 2 * (pr % 4);
+        const uint32_t at = smem0 + C::kQOff + u * C::kFragBytes + ((h + 16 * kg) * 8 + j) * C::kSz;
+        if constexpr (std::is_same<T, bf16>::value) {
+          typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          bf16x2 v;
+          v[0] = from_f32<bf16>(x0 * a.qk_scale_log2);
+          v[1] = from_f32<bf16>(x1 * a.qk_scale_log2);
+          lds_st<bf16x2>(at, v);
+        } else {
+          lds_st<f32x2>(at, f32x2{x0 * a.qk_scale_log2, x1 * a.qk_scale_log2});
+        }
+      }
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < G * D / 2; i += kThreads) {
-      const int h = i / (D / 2), pr = i % (D / 2);
-      float x0 = to_f32(q[h * D + 2 * pr]) * rstd_s[h] * to_f32(gq[2 * pr]);
-      float x1 = to_f32(q[h * D + 2 * pr + 1]) * rstd_s[h] * to_f32(gq[2 * pr + 1]);
-      if (pr < a.n_rot) rotate_pair(x0, x1, qcs[pr]);
-      q_s[h][2 * pr] = x0 * a.qk_scale_log2;
-      q_s[h][2 * pr + 1] = x1 * a.qk_scale_log2;
-    }
-    __syncthreads();
   }
-  const int hcol = lane & 15, kg = lane >> 4;
-  Frag8<T> qf[C::kQSteps];
-#pragma unroll
-  for (int u = 0; u < C::kQSteps; ++u)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) frag_set(qf[u], j, hcol < G ? q_s[hcol][32 * u + 8 * kg + j] : 0.f);
 
   // ---- K=V rotation factors ------------------------------------------------------
   // The lane's rotated QK^T fragments hold key (key0 + hcol) at pairs
   // i = 16u + 4kg + p (u < kRotSteps, p < 4).  cos/sin((key0 + hcol) w_i) =
-  // coarse(key0 w_i) (x) fine(hcol w_i): fine stays in registers; coarse is
-  // kept per pair (lane = pair), stepped by 16 w_i each tile and shared
-  // through LDS.
-  f32x2 fine[SHARED ? C::kRotSteps * 4 : 1];
+  // coarse(key0 w_i) (x) fine(hcol w_i): fine is a table shared by the
+  // workgroup; coarse is kept per pair (lane = pair), stepped by 16 w_i each
+  // tile and published to the wave through LDS.
   f32x2 coarse_l{}, step_l{};
+  const uint32_t coarse_s = smem0 + C::kCoarseOff + wave * C::kCoarseBytes;
   if constexpr (SHARED) {
-#pragma unroll
-    for (int u = 0; u < C::kRotSteps; ++u)
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        fine[4 * u + p] = rope_cos_sin(static_cast<double>(hcol) * rope_omega(16 * u + 4 * kg + p, D, a.log2_theta));
+    for (int i = threadIdx.x; i < 16 * C::kRot; i += kThreads) {
+      const int j = i / C::kRot, pr = i % C::kRot;
+      lds_st<f32x2>(smem0 + C::kFineOff + i * 8,
+                    rope_cos_sin(static_cast<double>(j) * rope_omega(pr, D, a.log2_theta)));
+    }
     const double w = rope_omega(lane, D, a.log2_theta);
     coarse_l = rope_cos_sin(static_cast<double>(w0) * w);
     step_l = rope_cos_sin(16.0 * w);
+    lds_st<f32x2>(coarse_s + lane * 8, coarse_l);     // first tile's angles
   }
+  __syncthreads();
 
   // ---- stream this wave's keys -----------------------------------------------------
+  const int hcol = lane & 15, kg = lane >> 4;
+  const uint32_t k_lane = key_lane_base<C, T>(tiles, lane);
+  const uint32_t v_lane = value_lane_base<C, T>(tiles + (SHARED ? 0 : C::kKBytes), lane);
+  const uint32_t q_lane = smem0 + C::kQOff + lane * 8 * C::kSz;
+  const uint32_t fine_lane = smem0 + C::kFineOff + (hcol * C::kRot + 4 * kg) * 8;
+  const uint32_t coarse_lane = coarse_s + 4 * kg * 8;
+
   f32x4 o[C::kDBlocks];
 #pragma unroll
   for (int t = 0; t < C::kDBlocks; ++t) o[t] = f32x4{};
   float m_run = -INFINITY, l_part = 0.f;
   constexpr float kTau = 8.0f;
+  constexpr int kQAhead = 2;   // QK^T steps whose LDS reads are in flight
+  constexpr int kVAhead = 8;   // PV blocks whose LDS reads are in flight
 
   for (int it = 0; it < ntiles; ++it) {
     const int key0 = w0 + it * C::KT;
-    const char* kt_lds = wlds + (it & 1) * C::kTileBytes;
-    const char* vt_lds = SHARED ? kt_lds : kt_lds + C::kKBytes;
+    const uint32_t buf = (it & 1) * C::kTileBytes;
     // tile `it` has landed once at most the next tile's copies are in flight
     if (it + 1 < ntiles) wait_vm_le<C::kDmaPerTile>();
     else wait_vm_le<0>();
 
-    // S^T = K~ Q~^T; the lane's A operand is key row hcol, dims 32u + 8kg .. +7
-    f32x4 s = f32x4{};
-    const char* krow = kt_lds + hcol * C::kRowBytes;
-    if constexpr (SHARED) {
-      coarse_s[lane] = coarse_l;
-      lds_fence();
+    // S^T = K~ Q~^T; the lane's A operand is key row hcol, dims 32u + 8kg .. +7.
+    // Reads run kQAhead steps ahead of the MFMAs.
+    QkStep<T> st[kQAhead + 1];
 #pragma unroll
-      for (int u = 0; u < C::kRotSteps; ++u) {
-        Frag8<T> kf;
-        row_frag(kf, krow, hcol, (32 * u + 8 * kg) * C::kSz / 16);
+    for (int u = 0; u < kQAhead; ++u) load_step<C>(st[u], u, k_lane + buf, q_lane, coarse_lane, fine_lane);
+    f32x4 sa = f32x4{}, sb = f32x4{};
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const f32x2 cb = coarse_s[16 * u + 4 * kg + p];
-          const f32x2 fj = fine[4 * u + p];
-          f32x2 cs;
-          cs[0] = cb[0] * fj[0] - cb[1] * fj[1];
-          cs[1] = cb[1] * fj[0] + cb[0] * fj[1];
-          float x0 = to_f32(kf.v[2 * p]), x1 = to_f32(kf.v[2 * p + 1]);
-          rotate_pair(x0, x1, cs);
-          frag_set(kf, 2 * p, x0);
-          frag_set(kf, 2 * p + 1, x1);
-        }
-        mma16(s, kf, qf[u]);
-      }
-      // next tile's coarse angle: advance by 16 positions
+    for (int u = 0; u < C::kQSteps; ++u) {
+      if (u + kQAhead < C::kQSteps)
+        load_step<C>(st[(u + kQAhead) % (kQAhead + 1)], u + kQAhead, k_lane + buf, q_lane, coarse_lane, fine_lane);
+      QkStep<T>& cur = st[u % (kQAhead + 1)];
+      if (u < C::kRotSteps) rotate_step(cur);
+      mma16((u & 1) ? sb : sa, cur.kf, cur.qf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    f32x4 s = sa + sb;
+    if constexpr (SHARED) {   // publish the next tile's coarse angles (16 positions on)
       const f32x2 c = coarse_l;
       coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
       coarse_l[1] = c[1] * step_l[0] + c[0] * step_l[1];
-    }
-#pragma unroll
-    for (int u = C::kRotSteps; u < C::kQSteps; ++u) {
-      Frag8<T> kf;
-      row_frag(kf, krow, hcol, (32 * u + 8 * kg) * C::kSz / 16);
-      mma16(s, kf, qf[u]);
+      lds_st<f32x2>(coarse_s + lane * 8, coarse_l);   // read next tile, after the fence below
     }
 
     // online softmax; lane holds keys 4*kg + v of head column hcol
@@ -265,8 +401,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
       if (key0 + 4 * kg + v >= w1) s[v] = -INFINITY;
       mt = fmaxf(mt, s[v]);
     }
-    mt = fmaxf(mt, wave_xor(mt, 16));
-    mt = fmaxf(mt, wave_xor(mt, 32));
+    mt = max_across_kg(mt);
     const bool rescale = __any(mt > m_run + kTau);
     const float m_new = rescale ? fmaxf(m_run, mt) : m_run;
     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -287,16 +422,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeArgs a) {
     }
     l_part += psum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T, reads kVAhead blocks ahead
+    Frag4<T> vf[kVAhead];
+#pragma unroll
+    for (int t = 0; t < kVAhead; ++t) value_frag<C>(vf[t], v_lane + buf, t);
 #pragma unroll
     for (int t = 0; t < C::kDBlocks; ++t) {
-      Frag4<T> vf;
-      vt_frag<C::kRowBytes>(vf, vt_lds, 16 * t, lane);
-      mma16k16(o[t], vf, pf);
+      const Frag4<T> cur = vf[t % kVAhead];
+      if (t + kVAhead < C::kDBlocks) value_frag<C>(vf[t % kVAhead], v_lane + buf, t + kVAhead);
+      mma16k16(o[t], cur, pf);
+      __builtin_amdgcn_sched_barrier(0);
     }
     lds_fence();   // this tile's LDS reads are done before its buffer is refilled
-    if (it + 2 < ntiles)
-      issue_tile<T, D, G, SHARED>(wlds + (it & 1) * C::kTileBytes, kbase, vbase, key0 + 2 * C::KT, nkeys, lane);
+    if (it + 2 < ntiles) issue_tile<C>(tiles + buf, rk, rv, key0 + 2 * C::KT, nkeys, lane);
   }
 
   // ---- merge the waves of this item ------------------------------------------------

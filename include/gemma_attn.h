@@ -151,6 +151,9 @@ size_t gemma_attn_decode_workspace_size(const ga_layer* layer, int32_t batch,
  *            output row instead of reading out of bounds.
  *   out      [B, Hq, d]
  *   workspace >= gemma_attn_decode_workspace_size() bytes, 256-byte aligned.
+ * GA_EUNSUPPORTED if one head's cache (cache_cap * d * element size) reaches
+ * 2 GiB, if max_seq_len needs more than 1024 chunks of 1024 positions, or for
+ * fp32 with d = 512 and a separate V cache.
  */
 ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch,
                             const void* q, const void* q_gain,
