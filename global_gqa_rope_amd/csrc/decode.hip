@@ -61,7 +61,7 @@ struct DecodeCfg {
   static constexpr int kQOff = kCoarseOff + kWaves * kCoarseBytes;
   static constexpr int kFineOff = kQOff + kQBytes;
   static constexpr int kLdsBytes = kFineOff + kFineBytes;
-  static constexpr int kCombineBytes = kWaves * (G * D + 32) * 4;   // reuses the tiles
+  static constexpr int kCombineBytes = (kWaves * (G * D + 32) + G * (kWaves + 2)) * 4;   // reuses the tiles
   static_assert(kLdsBytes <= kLdsLimit, "LDS budget");
   static_assert(kCombineBytes <= kCoarseOff, "wave combine area must fit in the tile area");
   static_assert(kRowBytes / 16 >= 16, "row swizzle needs 16 chunks per row");
@@ -204,7 +204,7 @@ __device__ __forceinline__ void load_qfrag(Frag8<float>& f, uint32_t a) {
 template <typename T>
 struct QkStep {
   Frag8<T> kf, qf;
-  f32x2 cb[4], fj[4];
+  f32x4 cb[2], fj[2];   // (cos, sin) of pairs p = 0, 1 and p = 2, 3
 };
 template <typename C, typename T>
 __device__ __forceinline__ void load_step(QkStep<T>& st, int u, uint32_t k_lane, uint32_t q_lane,
@@ -213,9 +213,9 @@ __device__ __forceinline__ void load_step(QkStep<T>& st, int u, uint32_t k_lane,
   load_qfrag(st.qf, q_lane + u * C::kFragBytes);
   if (u < C::kRotSteps) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      st.cb[p] = lds_ld<f32x2>(coarse_lane + (16 * u + p) * 8);
-      st.fj[p] = lds_ld<f32x2>(fine_lane + (16 * u + p) * 8);
+    for (int h = 0; h < 2; ++h) {
+      st.cb[h] = lds_ld<f32x4>(coarse_lane + (16 * u + 2 * h) * 8);
+      st.fj[h] = lds_ld<f32x4>(fine_lane + (16 * u + 2 * h) * 8);
     }
   }
 }
@@ -224,14 +224,27 @@ template <typename T>
 __device__ __forceinline__ void rotate_step(QkStep<T>& st) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
+    const f32x4& cb4 = st.cb[p >> 1];
+    const f32x4& fj4 = st.fj[p >> 1];
+    const int o = 2 * (p & 1);
     f32x2 cs;
-    cs[0] = st.cb[p][0] * st.fj[p][0] - st.cb[p][1] * st.fj[p][1];
-    cs[1] = st.cb[p][1] * st.fj[p][0] + st.cb[p][0] * st.fj[p][1];
+    cs[0] = cb4[o] * fj4[o] - cb4[o + 1] * fj4[o + 1];
+    cs[1] = cb4[o + 1] * fj4[o] + cb4[o] * fj4[o + 1];
     float x0 = to_f32(st.kf.v[2 * p]), x1 = to_f32(st.kf.v[2 * p + 1]);
     rotate_pair(x0, x1, cs);
     frag_set(st.kf, 2 * p, x0);
     frag_set(st.kf, 2 * p + 1, x1);
   }
+}
+
+// Sum over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_across_kg(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const unsigned v = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 // Max over the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48),
@@ -279,49 +292,58 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
   if (ntiles > 0) issue_tile<C>(tiles, rk, rv, w0, nkeys, lane);
   if (ntiles > 1) issue_tile<C>(tiles + C::kTileBytes, rk, rv, w0 + C::KT, nkeys, lane);
 
+  // ---- rotation rates of the lane's pairs lane + 64 m (fp64, one exp2 each) ------
+  constexpr int kPairsPerLane = D / 128;
+  double w_pair[kPairsPerLane];
+#pragma unroll
+  for (int m = 0; m < kPairsPerLane; ++m)
+    w_pair[m] = (lane + 64 * m < a.n_rot) ? rope_omega(lane + 64 * m, D, a.log2_theta) : 0.0;
+
   // ---- query prep: QKNorm + rotation at qpos, written in operand order --------
   // Operand fragment u, lane hcol + 16 kg, element j = q~[hcol][32u + 8kg + j]
   // (heads >= G are zeros).  One wave per head: lane owns pairs lane + 64 m.
   {
-    constexpr int kPairsPerLane = D / 128;
     const T* __restrict__ q = static_cast<const T*>(a.q) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G) * D;
     const T* __restrict__ gq = static_cast<const T*>(a.q_gain);
     f32x2 qcs[kPairsPerLane];
 #pragma unroll
-    for (int m = 0; m < kPairsPerLane; ++m) {
-      const int pr = lane + 64 * m;
-      qcs[m] = pr < a.n_rot ? rope_cos_sin(static_cast<double>(qpos) * rope_omega(pr, D, a.log2_theta))
-                            : f32x2{1.f, 0.f};
-    }
+    for (int m = 0; m < kPairsPerLane; ++m)
+      qcs[m] = (lane + 64 * m < a.n_rot) ? rope_cos_sin(static_cast<double>(qpos) * w_pair[m]) : f32x2{1.f, 0.f};
     for (int h = wave; h < 16; h += C::kWaves) {
       float x[kPairsPerLane][2];
-      float ss = 0.f;
+      float rstd = 0.f;
+      if (h < G) {
+        float ss = 0.f;
 #pragma unroll
-      for (int m = 0; m < kPairsPerLane; ++m) {
-        const int pr = lane + 64 * m;
-        x[m][0] = h < G ? to_f32(q[h * D + 2 * pr]) : 0.f;
-        x[m][1] = h < G ? to_f32(q[h * D + 2 * pr + 1]) : 0.f;
-        ss += x[m][0] * x[m][0] + x[m][1] * x[m][1];
+        for (int m = 0; m < kPairsPerLane; ++m) {
+          const int pr = lane + 64 * m;
+          x[m][0] = to_f32(q[h * D + 2 * pr]);
+          x[m][1] = to_f32(q[h * D + 2 * pr + 1]);
+          ss += x[m][0] * x[m][0] + x[m][1] * x[m][1];
+        }
+#pragma unroll
+        for (int s = 1; s < 64; s <<= 1) ss += wave_xor(ss, s);
+        rstd = 1.0f / sqrtf(ss / D + a.eps) * a.qk_scale_log2;
       }
 #pragma unroll
-      for (int s = 1; s < 64; s <<= 1) ss += wave_xor(ss, s);
-      const float rstd = 1.0f / sqrtf(ss / D + a.eps);
-#pragma unroll
       for (int m = 0; m < kPairsPerLane; ++m) {
         const int pr = lane + 64 * m;
-        float x0 = x[m][0] * rstd * to_f32(gq[2 * pr]);
-        float x1 = x[m][1] * rstd * to_f32(gq[2 * pr + 1]);
-        rotate_pair(x0, x1, qcs[m]);
+        float x0 = 0.f, x1 = 0.f;
+        if (h < G) {
+          x0 = x[m][0] * rstd * to_f32(gq[2 * pr]);
+          x1 = x[m][1] * rstd * to_f32(gq[2 * pr + 1]);
+          rotate_pair(x0, x1, qcs[m]);
+        }
         const int u = pr / 16, kg = (pr % 16) / 4, j = 2 * (pr % 4);
         const uint32_t at = smem0 + C::kQOff + u * C::kFragBytes + ((h + 16 * kg) * 8 + j) * C::kSz;
         if constexpr (std::is_same<T, bf16>::value) {
           typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
           bf16x2 v;
-          v[0] = from_f32<bf16>(x0 * a.qk_scale_log2);
-          v[1] = from_f32<bf16>(x1 * a.qk_scale_log2);
+          v[0] = from_f32<bf16>(x0);
+          v[1] = from_f32<bf16>(x1);
           lds_st<bf16x2>(at, v);
         } else {
-          lds_st<f32x2>(at, f32x2{x0 * a.qk_scale_log2, x1 * a.qk_scale_log2});
+          lds_st<f32x2>(at, f32x2{x0, x1});
         }
       }
     }
@@ -332,18 +354,24 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
   // i = 16u + 4kg + p (u < kRotSteps, p < 4).  cos/sin((key0 + hcol) w_i) =
   // coarse(key0 w_i) (x) fine(hcol w_i): fine is a table shared by the
   // workgroup; coarse is kept per pair (lane = pair), stepped by 16 w_i each
-  // tile and published to the wave through LDS.
+  // tile and published to the wave through LDS.  Only the coarse start angle
+  // is large (up to the context length in radians) and needs fp64 sine and
+  // cosine; fine and step angles are below 16 rad, where fp32 sincosf of the
+  // fp32-rounded angle is accurate to about 1e-6.
   f32x2 coarse_l{}, step_l{};
   const uint32_t coarse_s = smem0 + C::kCoarseOff + wave * C::kCoarseBytes;
   if constexpr (SHARED) {
+    static_assert(kThreads % 64 == 0 && C::kRot == 64, "fine table: thread t fills pair t % 64");
+    const double w = w_pair[0];               // pair = lane
     for (int i = threadIdx.x; i < 16 * C::kRot; i += kThreads) {
-      const int j = i / C::kRot, pr = i % C::kRot;
-      lds_st<f32x2>(smem0 + C::kFineOff + i * 8,
-                    rope_cos_sin(static_cast<double>(j) * rope_omega(pr, D, a.log2_theta)));
+      float sn, cs;
+      sincosf(static_cast<float>((i / C::kRot) * w), &sn, &cs);
+      lds_st<f32x2>(smem0 + C::kFineOff + i * 8, f32x2{cs, sn});
     }
-    const double w = rope_omega(lane, D, a.log2_theta);
     coarse_l = rope_cos_sin(static_cast<double>(w0) * w);
-    step_l = rope_cos_sin(16.0 * w);
+    float sn, cs;
+    sincosf(static_cast<float>(16.0 * w), &sn, &cs);
+    step_l = f32x2{cs, sn};
     lds_st<f32x2>(coarse_s + lane * 8, coarse_l);     // first tile's angles
   }
   __syncthreads();
@@ -438,43 +466,59 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
   }
 
   // ---- merge the waves of this item ------------------------------------------------
-  float l = l_part + wave_xor(l_part, 16);
-  l += wave_xor(l, 32);
-  __syncthreads();
-  float* comb = reinterpret_cast<float*>(smem);          // [wave][G*D + 32]
-  float* mine = comb + wave * (G * D + 32);
+  // comb: [wave][G][D] outputs | [wave][32] (m per head, l per head) | [G][kWaves]
+  // weights exp2(m_w - M) (divided by the item's sum when it is the only chunk)
+  // | [G][2] (M, L).
+  const float l = sum_across_kg(l_part);
+  __syncthreads();                                          // tiles are no longer read
+  float* comb = reinterpret_cast<float*>(smem);
+  float* ml = comb + C::kWaves * G * D;
+  float* wts = ml + C::kWaves * 32;
+  float* stats = wts + G * C::kWaves;
   if (hcol < G) {
+    float* mine = comb + (wave * G + hcol) * D + 4 * kg;
 #pragma unroll
-    for (int t = 0; t < C::kDBlocks; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) mine[hcol * D + 16 * t + 4 * kg + v] = o[t][v];
+    for (int t = 0; t < C::kDBlocks; ++t) *reinterpret_cast<f32x4*>(mine + 16 * t) = o[t];
     if (kg == 0) {
-      mine[G * D + hcol] = m_run;
-      mine[G * D + 16 + hcol] = l;
+      ml[wave * 32 + hcol] = m_run;
+      ml[wave * 32 + 16 + hcol] = l;
     }
   }
   __syncthreads();
-  float* part = a.partials + ((head * a.n_chunks + chunk) * G) * (D + 2);
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int h = i / D, d = i % D;
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
     float M = -INFINITY;
-    for (int w = 0; w < C::kWaves; ++w) M = fmaxf(M, comb[w * (G * D + 32) + G * D + h]);
-    float L = 0.f, O = 0.f;
+    for (int w = 0; w < C::kWaves; ++w) M = fmaxf(M, ml[w * 32 + h]);
+    float L = 0.f;
+    float e[C::kWaves];
+#pragma unroll
     for (int w = 0; w < C::kWaves; ++w) {
-      const float* cw = comb + w * (G * D + 32);
-      const float mw = cw[G * D + h];
-      const float e = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L += e * cw[G * D + 16 + h];
-      O += e * cw[h * D + d];
+      const float mw = ml[w * 32 + h];
+      e[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += e[w] * ml[w * 32 + 16 + h];
     }
+    const float scale = (n_chunks == 1) ? 1.0f / L : 1.0f;
+#pragma unroll
+    for (int w = 0; w < C::kWaves; ++w) wts[h * C::kWaves + w] = e[w] * scale;
+    stats[2 * h] = M;
+    stats[2 * h + 1] = L;
+  }
+  __syncthreads();
+  float* part = a.partials + ((head * a.n_chunks + chunk) * G) * (D + 2);
+  for (int g4 = threadIdx.x; g4 < G * D / 4; g4 += kThreads) {
+    const int h = g4 / (D / 4), d = 4 * (g4 % (D / 4));
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int w = 0; w < C::kWaves; ++w)
+      acc += wts[h * C::kWaves + w] * *reinterpret_cast<const f32x4*>(comb + (w * G + h) * D + d);
     if (n_chunks == 1) {
-      out[h * D + d] = from_f32<T>(O / L);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) out[h * D + d + v] = from_f32<T>(acc[v]);
     } else {
-      part[h * (D + 2) + 2 + d] = O;
-      if (d == 0) {
-        part[h * (D + 2)] = M;
-        part[h * (D + 2) + 1] = L;
-      }
+      float* dst = part + h * (D + 2) + 2 + d;              // 8-byte aligned
+      *reinterpret_cast<f32x2*>(dst) = f32x2{acc[0], acc[1]};
+      *reinterpret_cast<f32x2*>(dst + 2) = f32x2{acc[2], acc[3]};
+      if (d == 0) *reinterpret_cast<f32x2*>(part + h * (D + 2)) = f32x2{stats[2 * h], stats[2 * h + 1]};
     }
   }
 }
