@@ -153,15 +153,25 @@ PrefillLayout prefill_layout(const ga_layer* L, const Derived& dv, int batch, in
   return p;
 }
 
-int decode_chunks(const ga_layer* L, int max_seq_len) {
+int decode_tiles_per_seq(const ga_layer* L, int max_seq_len) {
   const int keys = L->window > 0 ? std::min(max_seq_len, L->window) : max_seq_len;
-  return (keys + ga::kDecodeChunk - 1) / ga::kDecodeChunk;
+  return (keys + ga::kDecodeTile - 1) / ga::kDecodeTile;
+}
+
+// Decode scratch is sized for the largest grid the launch can pick (at most
+// 1024 waves' partial slots plus one per wave and segment), so it does not
+// depend on the device; the launch then uses one workgroup per CU at most.
+constexpr int kMaxDecodeCUs = 1 << 20;
+
+bool decode_plan(const ga_layer* L, const Derived& dv, int batch, int max_seq_len, int n_cus, ga::DecodePlan* plan) {
+  return ga::plan_decode(L->dtype, L->head_dim, dv.group, L->kv_shared, batch, L->n_kv_heads,
+                         decode_tiles_per_seq(L, max_seq_len), n_cus, plan);
 }
 
 size_t decode_bytes(const ga_layer* L, const Derived& dv, int batch, int max_seq_len) {
-  const int n = decode_chunks(L, max_seq_len);
-  if (n <= 1) return 0;
-  return align_up(static_cast<size_t>(batch) * L->n_kv_heads * n * dv.group * (L->head_dim + 2) * 4);
+  ga::DecodePlan plan;
+  if (!decode_plan(L, dv, batch, max_seq_len, kMaxDecodeCUs, &plan)) return 0;
+  return align_up(plan.bytes());
 }
 
 ga_status check_workspace(void* ws, size_t have, size_t need) {
@@ -316,9 +326,9 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
   if (batch < 0) return fail(GA_EINVAL, "batch must be >= 0");
   if (batch == 0) return GA_OK;
   if (max_seq_len < 1) return fail(GA_EINVAL, "max_seq_len must be >= 1");
-  if (decode_chunks(layer, max_seq_len) > 1024)
-    return fail(GA_EUNSUPPORTED, "max_seq_len %d: decode supports up to %d cached positions", max_seq_len,
-                1024 * ga::kDecodeChunk);
+  if (static_cast<int64_t>(batch) * layer->n_kv_heads * decode_tiles_per_seq(layer, max_seq_len) > INT32_MAX)
+    return fail(GA_EUNSUPPORTED, "batch %d x max_seq_len %d: too many cached positions for one decode call", batch,
+                max_seq_len);
   if (!q || !q_gain || !seq_lens || !out) return fail(GA_EINVAL, "q, q_gain, seq_lens and out must be non-NULL");
   if (layer->dtype == GA_F32 && layer->head_dim == 512 && !layer->kv_shared)
     return fail(GA_EUNSUPPORTED, "fp32 decode with head_dim 512 and a separate V cache is not built");
@@ -329,12 +339,21 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
   const size_t need = decode_bytes(layer, dv, batch, max_seq_len);
   st = check_workspace(workspace, workspace_bytes, need);
   if (st != GA_OK) return st;
+  int dev = 0, cus = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he == hipSuccess) he = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (he != hipSuccess) return hip_status(he, "decode: device query");
+  ga::DecodePlan plan;
+  if (!decode_plan(layer, dv, batch, max_seq_len, cus, &plan))
+    return fail(GA_EUNSUPPORTED, "no decode kernel for this layer configuration");
   ga::DecodeArgs da{};
   da.q = q; da.q_gain = q_gain; da.k_cache = k_cache; da.v_cache = v_cache; da.seq_lens = seq_lens;
-  da.out = out; da.partials = static_cast<float*>(workspace); da.n_q_heads = layer->n_q_heads;
-  da.n_kv_heads = layer->n_kv_heads; da.n_rot = dv.n_rot; da.window = layer->window; da.cache_cap = cache_cap;
-  da.max_seq_len = max_seq_len; da.n_chunks = decode_chunks(layer, max_seq_len); da.eps = layer->norm_eps;
-  da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
+  da.out = out;
+  da.tile_prefix = static_cast<int32_t*>(workspace);
+  da.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.prefix_bytes);
+  da.batch = batch; da.n_q_heads = layer->n_q_heads; da.n_kv_heads = layer->n_kv_heads; da.n_rot = dv.n_rot;
+  da.window = layer->window; da.cache_cap = cache_cap; da.max_seq_len = max_seq_len; da.n_wgs = plan.n_wgs;
+  da.eps = layer->norm_eps; da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
   return hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
                                       static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),
                     "decode launch");

@@ -1,7 +1,9 @@
 // Split-K decode: one query token per sequence against its cache, gfx950.
 //
-// Work item = (chunk of kDecodeChunk cached positions, KV head, sequence).  Each
-// wave of the workgroup streams its share of the chunk in tiles of 16 keys:
+// A persistent grid: one workgroup per CU takes an equal, contiguous share of
+// all 16-key tiles of all (sequence, KV head) segments, so every CU streams
+// the same number of bytes and keeps streaming across segment boundaries.
+// Each wave of the workgroup takes every kWaves-th tile of that share:
 //   global -> LDS by buffer loads that write LDS directly, two tiles per wave,
 //   the next tile in flight while the current one is computed;
 //   K=V layers: pairs 0..63 of every key are rotated on the fly as they are
@@ -10,13 +12,14 @@
 //   ("K=V" section of the same page);
 //   S^T[key][head] = K~ Q~^T   (16x16x32 MFMA, the G heads padded to 16 columns;
 //                               the query operand is read from LDS, where the
-//                               workgroup wrote it once in operand order)
+//                               workgroup writes it once per segment in operand
+//                               order)
 //   online softmax per head (exp2 domain, lazy rescale)
 //   O^T[d][head] += V^T P^T     (16x16x16 MFMA; V^T by LDS transpose reads, P
 //                               straight from the S^T registers)
-// The waves then merge through LDS into one partial (max, sum, o) per item, or
-// the final row when the item is the sequence's only chunk; a second kernel
-// merges the partials of longer sequences by log-sum-exp.
+// Every wave leaves one partial (o, max, sum) per segment it took part in; a
+// second kernel merges the partials of each (sequence, query head) by
+// log-sum-exp.
 //
 // All LDS addressing inside the loop is one XOR per read: tiles sit at
 // multiples of their size and rows at multiples of the row size, and a
@@ -49,21 +52,20 @@ struct DecodeCfg {
   static constexpr int kFineBytes = 16 * kRot * 8;    // cos/sin(j w_i), j < 16, i < kRot
   static constexpr int kCoarseBytes = kRot * 8;       // per wave: cos/sin(key0 w_i)
   static constexpr int kPerWaveBytes = kBufs * kTileBytes + kCoarseBytes;
-  static constexpr int kCommonBytes = kQBytes + kFineBytes;
+  static constexpr int kMiscBytes = 64;               // partition scratch
+  static constexpr int kCommonBytes = kQBytes + kFineBytes + kMiscBytes;
   static constexpr int kWaves = (4 * kPerWaveBytes + kCommonBytes <= kLdsLimit)   ? 4
                                 : (2 * kPerWaveBytes + kCommonBytes <= kLdsLimit) ? 2
                                                                                   : 1;
-  static constexpr int kPerWave = kDecodeChunk / kWaves;
   static constexpr int kDmaPerTile = kTileBytes / 1024;
   static constexpr int kKDma = kKBytes / 1024;
-  // LDS map: [wave][buf] tiles | [wave] coarse angles | query operand | fine angles
+  // LDS map: [wave][buf] tiles | [wave] coarse angles | query operand | fine angles | misc
   static constexpr int kCoarseOff = kWaves * kBufs * kTileBytes;
   static constexpr int kQOff = kCoarseOff + kWaves * kCoarseBytes;
   static constexpr int kFineOff = kQOff + kQBytes;
-  static constexpr int kLdsBytes = kFineOff + kFineBytes;
-  static constexpr int kCombineBytes = (kWaves * (G * D + 32) + G * (kWaves + 2)) * 4;   // reuses the tiles
+  static constexpr int kMiscOff = kFineOff + kFineBytes;
+  static constexpr int kLdsBytes = kMiscOff + kMiscBytes;
   static_assert(kLdsBytes <= kLdsLimit, "LDS budget");
-  static_assert(kCombineBytes <= kCoarseOff, "wave combine area must fit in the tile area");
   static_assert(kRowBytes / 16 >= 16, "row swizzle needs 16 chunks per row");
   static_assert(kTileBytes % 1024 == 0 && kDmaPerTile < 64, "tile copy");
 };
@@ -258,39 +260,122 @@ __device__ __forceinline__ float max_across_kg(float x) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
+// ---- work partition ---------------------------------------------------------------
+// Segment s = b * Hkv + kvh holds sequence b's readable keys for KV head kvh,
+// n_b = ceil(keys_b / 16) tiles (none for an invalid length).  Segments sit end
+// to end in tile order, segment s starting at tile T_s = Hkv * prefix_b + kvh * n_b.
+// Workgroup w of P takes tiles [floor(T w / P), floor(T (w + 1) / P)) of the T
+// in total, so every workgroup streams the same number of tiles (+-1).
+__device__ __forceinline__ int seq_tiles(const DecodeArgs& a, int b) {
+  const int keys = decode_keys(a, b);
+  return keys > 0 ? (keys + kDecodeTile - 1) / kDecodeTile : 0;
+}
+
+// Wave-uniform cursor over segments, moved forward only.
+struct Seg {
+  int b, kvh, T, n, keys;
+};
+__device__ __forceinline__ void seg_next(Seg& g, const DecodeArgs& a) {
+  g.T += g.n;
+  if (++g.kvh == a.n_kv_heads) {
+    g.kvh = 0;
+    ++g.b;
+    g.keys = g.b < a.batch ? decode_keys(a, g.b) : 0;
+    g.n = g.keys > 0 ? (g.keys + kDecodeTile - 1) / kDecodeTile : 0;
+  }
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 template <typename T, int D, int G, bool SHARED>
 __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, G, SHARED>;
+  static_assert(C::KT == kDecodeTile, "tile size");
+  constexpr int kSlot = G * D + 64;
   __shared__ __attribute__((aligned(4096))) char smem[C::kLdsBytes];
 
-  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int wg = blockIdx.x, P = gridDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   constexpr int kThreads = C::kWaves * 64;
-  const int nkeys = decode_keys(a, b);
-  T* __restrict__ out = static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G) * D;
-  if (nkeys < 0) {
-    if (chunk == 0)
-      for (int i = threadIdx.x; i < G * D; i += kThreads) out[i] = from_f32<T>(NAN);
-    return;
-  }
-  const int c0 = chunk * kDecodeChunk;
-  if (c0 >= nkeys) return;
-  const int n_chunks = (nkeys + kDecodeChunk - 1) / kDecodeChunk;
-  const int qpos = a.seq_lens[b] - 1;
+  int* misc = reinterpret_cast<int*>(smem + C::kMiscOff);
 
-  // ---- stream setup: start this wave's first two tile copies right away -----
-  const int64_t head = static_cast<int64_t>(b) * a.n_kv_heads + kvh;
-  const uint32_t span = static_cast<uint32_t>(a.cache_cap) * C::kRowBytes;   // < 2^31 (checked on the host)
-  const BufRsrc rk = make_rsrc(static_cast<const char*>(a.k_cache) + head * span, span);
-  const BufRsrc rv = SHARED ? rk : make_rsrc(static_cast<const char*>(a.v_cache) + head * span, span);
+  // ---- partition: total tiles, then this workgroup's first segment -----------------
+  int total = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += kThreads) {
+    const int bb = b0 + static_cast<int>(threadIdx.x);
+    const int n = wave_sum_i(bb < a.batch ? seq_tiles(a, bb) : 0);
+    if (lane == 0) misc[wave] = n;
+    __syncthreads();
+    for (int i = 0; i < C::kWaves; ++i) total += misc[i];
+    __syncthreads();
+  }
+  const int t_all = a.n_kv_heads * total;
+  const int t_begin = static_cast<int>(static_cast<int64_t>(t_all) * wg / P);
+  const int t_end = static_cast<int>(static_cast<int64_t>(t_all) * (wg + 1) / P);
+  int run = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += kThreads) {
+    const int bb = b0 + static_cast<int>(threadIdx.x);
+    const int n = bb < a.batch ? seq_tiles(a, bb) : 0;
+    const int incl = wave_incl_scan_i(n, lane);
+    if (lane == 63) misc[wave] = incl;
+    __syncthreads();
+    int before = run, block = 0;
+    for (int i = 0; i < C::kWaves; ++i) {
+      before += (i < wave) ? misc[i] : 0;
+      block += misc[i];
+    }
+    if (bb < a.batch) {
+      const int excl = before + incl - n;
+      if (wg == 0) a.tile_prefix[bb] = excl;
+      const int lo = a.n_kv_heads * excl;
+      if (n > 0 && t_begin >= lo && t_begin < lo + a.n_kv_heads * n) {
+        misc[8] = bb;
+        misc[9] = (t_begin - lo) / n;
+        misc[10] = lo;
+      }
+    }
+    run += block;
+    __syncthreads();
+  }
+  if (wg == 0 && threadIdx.x == 0) a.tile_prefix[a.batch] = run;
+  if (t_begin >= t_end) return;
+  Seg cur;
+  cur.b = misc[8];
+  cur.kvh = misc[9];
+  cur.keys = decode_keys(a, cur.b);
+  cur.n = (cur.keys + C::KT - 1) / C::KT;
+  cur.T = misc[10] + cur.kvh * cur.n;
+
+  // ---- tile stream: the wave's k-th tile is global tile t_begin + wave + kWaves k,
+  // copied into buffer k & 1; copies run two tiles ahead, across segments --------
   const uint32_t smem0 = lds_addr(smem);
   const uint32_t tiles = smem0 + wave * C::kBufs * C::kTileBytes;
-  const int w0 = c0 + wave * C::kPerWave;
-  const int w1 = min(w0 + C::kPerWave, nkeys);
-  const int ntiles = w1 > w0 ? (w1 - w0 + C::KT - 1) / C::KT : 0;
-  if (ntiles > 0) issue_tile<C>(tiles, rk, rv, w0, nkeys, lane);
-  if (ntiles > 1) issue_tile<C>(tiles + C::kTileBytes, rk, rv, w0 + C::KT, nkeys, lane);
+  const uint32_t span = static_cast<uint32_t>(a.cache_cap) * C::kRowBytes;   // < 2^31 (checked on the host)
+  Seg pf = cur;
+  auto issue = [&](int k) {
+    const int g = t_begin + wave + C::kWaves * k;
+    if (g >= t_end) return;
+    while (g >= pf.T + pf.n) seg_next(pf, a);
+    const int64_t head = static_cast<int64_t>(pf.b) * a.n_kv_heads + pf.kvh;
+    const BufRsrc rk = make_rsrc(static_cast<const char*>(a.k_cache) + head * span, span);
+    const BufRsrc rv = SHARED ? rk : make_rsrc(static_cast<const char*>(a.v_cache) + head * span, span);
+    issue_tile<C>(tiles + (k & 1) * C::kTileBytes, rk, rv, (g - pf.T) * C::KT, pf.keys, lane);
+  };
+  issue(0);
+  issue(1);
 
   // ---- rotation rates of the lane's pairs lane + 64 m (fp64, one exp2 each) ------
   constexpr int kPairsPerLane = D / 128;
@@ -299,250 +384,239 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
   for (int m = 0; m < kPairsPerLane; ++m)
     w_pair[m] = (lane + 64 * m < a.n_rot) ? rope_omega(lane + 64 * m, D, a.log2_theta) : 0.0;
 
-  // ---- query prep: QKNorm + rotation at qpos, written in operand order --------
-  // Operand fragment u, lane hcol + 16 kg, element j = q~[hcol][32u + 8kg + j]
-  // (heads >= G are zeros).  One wave per head: lane owns pairs lane + 64 m.
-  {
-    const T* __restrict__ q = static_cast<const T*>(a.q) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G) * D;
-    const T* __restrict__ gq = static_cast<const T*>(a.q_gain);
-    f32x2 qcs[kPairsPerLane];
-#pragma unroll
-    for (int m = 0; m < kPairsPerLane; ++m)
-      qcs[m] = (lane + 64 * m < a.n_rot) ? rope_cos_sin(static_cast<double>(qpos) * w_pair[m]) : f32x2{1.f, 0.f};
-    for (int h = wave; h < 16; h += C::kWaves) {
-      float x[kPairsPerLane][2];
-      float rstd = 0.f;
-      if (h < G) {
-        float ss = 0.f;
-#pragma unroll
-        for (int m = 0; m < kPairsPerLane; ++m) {
-          const int pr = lane + 64 * m;
-          x[m][0] = to_f32(q[h * D + 2 * pr]);
-          x[m][1] = to_f32(q[h * D + 2 * pr + 1]);
-          ss += x[m][0] * x[m][0] + x[m][1] * x[m][1];
-        }
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) ss += wave_xor(ss, s);
-        rstd = 1.0f / sqrtf(ss / D + a.eps) * a.qk_scale_log2;
-      }
-#pragma unroll
-      for (int m = 0; m < kPairsPerLane; ++m) {
-        const int pr = lane + 64 * m;
-        float x0 = 0.f, x1 = 0.f;
-        if (h < G) {
-          x0 = x[m][0] * rstd * to_f32(gq[2 * pr]);
-          x1 = x[m][1] * rstd * to_f32(gq[2 * pr + 1]);
-          rotate_pair(x0, x1, qcs[m]);
-        }
-        const int u = pr / 16, kg = (pr % 16) / 4, j = 2 * (pr % 4);
-        const uint32_t at = smem0 + C::kQOff + u * C::kFragBytes + ((h + 16 * kg) * 8 + j) * C::kSz;
-        if constexpr (std::is_same<T, bf16>::value) {
-          typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-          bf16x2 v;
-          v[0] = from_f32<bf16>(x0);
-          v[1] = from_f32<bf16>(x1);
-          lds_st<bf16x2>(at, v);
-        } else {
-          lds_st<f32x2>(at, f32x2{x0, x1});
-        }
-      }
-    }
-  }
-
   // ---- K=V rotation factors ------------------------------------------------------
   // The lane's rotated QK^T fragments hold key (key0 + hcol) at pairs
   // i = 16u + 4kg + p (u < kRotSteps, p < 4).  cos/sin((key0 + hcol) w_i) =
   // coarse(key0 w_i) (x) fine(hcol w_i): fine is a table shared by the
-  // workgroup; coarse is kept per pair (lane = pair), stepped by 16 w_i each
-  // tile and published to the wave through LDS.  Only the coarse start angle
-  // is large (up to the context length in radians) and needs fp64 sine and
-  // cosine; fine and step angles are below 16 rad, where fp32 sincosf of the
-  // fp32-rounded angle is accurate to about 1e-6.
+  // workgroup; coarse is kept per pair (lane = pair), stepped by the wave's
+  // tile stride (kWaves * 16 positions) each tile and published to the wave
+  // through LDS.  Only the coarse start angle is large (up to the context
+  // length in radians) and needs fp64 sine and cosine; fine and step angles are
+  // below 64 rad, where fp32 sincosf of the fp32-rounded angle is accurate to a
+  // few 1e-6.
   f32x2 coarse_l{}, step_l{};
   const uint32_t coarse_s = smem0 + C::kCoarseOff + wave * C::kCoarseBytes;
   if constexpr (SHARED) {
     static_assert(kThreads % 64 == 0 && C::kRot == 64, "fine table: thread t fills pair t % 64");
-    const double w = w_pair[0];               // pair = lane
     for (int i = threadIdx.x; i < 16 * C::kRot; i += kThreads) {
       float sn, cs;
-      sincosf(static_cast<float>((i / C::kRot) * w), &sn, &cs);
+      sincosf(static_cast<float>((i / C::kRot) * w_pair[0]), &sn, &cs);
       lds_st<f32x2>(smem0 + C::kFineOff + i * 8, f32x2{cs, sn});
     }
-    coarse_l = rope_cos_sin(static_cast<double>(w0) * w);
     float sn, cs;
-    sincosf(static_cast<float>(16.0 * w), &sn, &cs);
+    sincosf(static_cast<float>(C::kWaves * C::KT * w_pair[0]), &sn, &cs);
     step_l = f32x2{cs, sn};
-    lds_st<f32x2>(coarse_s + lane * 8, coarse_l);     // first tile's angles
   }
-  __syncthreads();
 
-  // ---- stream this wave's keys -----------------------------------------------------
   const int hcol = lane & 15, kg = lane >> 4;
   const uint32_t k_lane = key_lane_base<C, T>(tiles, lane);
   const uint32_t v_lane = value_lane_base<C, T>(tiles + (SHARED ? 0 : C::kKBytes), lane);
   const uint32_t q_lane = smem0 + C::kQOff + lane * 8 * C::kSz;
   const uint32_t fine_lane = smem0 + C::kFineOff + (hcol * C::kRot + 4 * kg) * 8;
   const uint32_t coarse_lane = coarse_s + 4 * kg * 8;
-
-  f32x4 o[C::kDBlocks];
-#pragma unroll
-  for (int t = 0; t < C::kDBlocks; ++t) o[t] = f32x4{};
-  float m_run = -INFINITY, l_part = 0.f;
   constexpr float kTau = 8.0f;
   constexpr int kQAhead = 2;   // QK^T steps whose LDS reads are in flight
   constexpr int kVAhead = 8;   // PV blocks whose LDS reads are in flight
+  const T* __restrict__ gq = static_cast<const T*>(a.q_gain);
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int key0 = w0 + it * C::KT;
-    const uint32_t buf = (it & 1) * C::kTileBytes;
-    // tile `it` has landed once at most the next tile's copies are in flight
-    if (it + 1 < ntiles) wait_vm_le<C::kDmaPerTile>();
-    else wait_vm_le<0>();
+  int k = 0;   // the wave's next tile
+  for (;;) {
+    const int seg = cur.b * a.n_kv_heads + cur.kvh;
+    const int p_end = min(cur.T + cur.n, t_end);
+    __syncthreads();   // the previous segment's reads of the query operand are done
 
-    // S^T = K~ Q~^T; the lane's A operand is key row hcol, dims 32u + 8kg .. +7.
-    // Reads run kQAhead steps ahead of the MFMAs.
-    QkStep<T> st[kQAhead + 1];
+    // ---- query prep: QKNorm + rotation at qpos, written in operand order ------
+    // Operand fragment u, lane hcol + 16 kg, element j = q~[hcol][32u + 8kg + j]
+    // (heads >= G are zeros).  One wave per head: lane owns pairs lane + 64 m.
+    {
+      const int qpos = a.seq_lens[cur.b] - 1;
+      const T* __restrict__ q =
+          static_cast<const T*>(a.q) + (static_cast<int64_t>(cur.b) * a.n_q_heads + cur.kvh * G) * D;
+      f32x2 qcs[kPairsPerLane];
 #pragma unroll
-    for (int u = 0; u < kQAhead; ++u) load_step<C>(st[u], u, k_lane + buf, q_lane, coarse_lane, fine_lane);
-    f32x4 sa = f32x4{}, sb = f32x4{};
+      for (int m = 0; m < kPairsPerLane; ++m)
+        qcs[m] = (lane + 64 * m < a.n_rot) ? rope_cos_sin(static_cast<double>(qpos) * w_pair[m]) : f32x2{1.f, 0.f};
+      for (int h = wave; h < 16; h += C::kWaves) {
+        float x[kPairsPerLane][2];
+        float rstd = 0.f;
+        if (h < G) {
+          float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < C::kQSteps; ++u) {
-      if (u + kQAhead < C::kQSteps)
-        load_step<C>(st[(u + kQAhead) % (kQAhead + 1)], u + kQAhead, k_lane + buf, q_lane, coarse_lane, fine_lane);
-      QkStep<T>& cur = st[u % (kQAhead + 1)];
-      if (u < C::kRotSteps) rotate_step(cur);
-      mma16((u & 1) ? sb : sa, cur.kf, cur.qf);
-      __builtin_amdgcn_sched_barrier(0);
+          for (int m = 0; m < kPairsPerLane; ++m) {
+            const int pr = lane + 64 * m;
+            x[m][0] = to_f32(q[h * D + 2 * pr]);
+            x[m][1] = to_f32(q[h * D + 2 * pr + 1]);
+            ss += x[m][0] * x[m][0] + x[m][1] * x[m][1];
+          }
+#pragma unroll
+          for (int sh = 1; sh < 64; sh <<= 1) ss += wave_xor(ss, sh);
+          rstd = 1.0f / sqrtf(ss / D + a.eps) * a.qk_scale_log2;
+        }
+#pragma unroll
+        for (int m = 0; m < kPairsPerLane; ++m) {
+          const int pr = lane + 64 * m;
+          float x0 = 0.f, x1 = 0.f;
+          if (h < G) {
+            x0 = x[m][0] * rstd * to_f32(gq[2 * pr]);
+            x1 = x[m][1] * rstd * to_f32(gq[2 * pr + 1]);
+            rotate_pair(x0, x1, qcs[m]);
+          }
+          const int u = pr / 16, g4 = (pr % 16) / 4, j = 2 * (pr % 4);
+          const uint32_t at = smem0 + C::kQOff + u * C::kFragBytes + ((h + 16 * g4) * 8 + j) * C::kSz;
+          if constexpr (std::is_same<T, bf16>::value) {
+            typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            bf16x2 v;
+            v[0] = from_f32<bf16>(x0);
+            v[1] = from_f32<bf16>(x1);
+            lds_st<bf16x2>(at, v);
+          } else {
+            lds_st<f32x2>(at, f32x2{x0, x1});
+          }
+        }
+      }
     }
-    f32x4 s = sa + sb;
-    if constexpr (SHARED) {   // publish the next tile's coarse angles (16 positions on)
-      const f32x2 c = coarse_l;
-      coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
-      coarse_l[1] = c[1] * step_l[0] + c[0] * step_l[1];
-      lds_st<f32x2>(coarse_s + lane * 8, coarse_l);   // read next tile, after the fence below
+    if constexpr (SHARED) {   // coarse angles of the wave's first tile in this segment
+      const int g = t_begin + wave + C::kWaves * k;
+      coarse_l = rope_cos_sin(static_cast<double>((g - cur.T) * C::KT) * w_pair[0]);
+      lds_st<f32x2>(coarse_s + lane * 8, coarse_l);
+    }
+    __syncthreads();   // query operand (and on the first pass the fine table) ready
+
+    f32x4 o[C::kDBlocks];
+#pragma unroll
+    for (int t = 0; t < C::kDBlocks; ++t) o[t] = f32x4{};
+    float m_run = -INFINITY, l_part = 0.f;
+
+    for (;; ++k) {
+      const int g = t_begin + wave + C::kWaves * k;
+      if (g >= p_end) break;
+      const int key0 = (g - cur.T) * C::KT;
+      const uint32_t buf = (k & 1) * C::kTileBytes;
+      // tile k has landed once at most the next tile's copies are in flight
+      if (g + C::kWaves < t_end) wait_vm_le<C::kDmaPerTile>();
+      else wait_vm_le<0>();
+
+      // S^T = K~ Q~^T; the lane's A operand is key row hcol, dims 32u + 8kg .. +7.
+      // Reads run kQAhead steps ahead of the MFMAs.
+      QkStep<T> st[kQAhead + 1];
+#pragma unroll
+      for (int u = 0; u < kQAhead; ++u) load_step<C>(st[u], u, k_lane + buf, q_lane, coarse_lane, fine_lane);
+      f32x4 sa = f32x4{}, sb = f32x4{};
+#pragma unroll
+      for (int u = 0; u < C::kQSteps; ++u) {
+        if (u + kQAhead < C::kQSteps)
+          load_step<C>(st[(u + kQAhead) % (kQAhead + 1)], u + kQAhead, k_lane + buf, q_lane, coarse_lane, fine_lane);
+        QkStep<T>& cs = st[u % (kQAhead + 1)];
+        if (u < C::kRotSteps) rotate_step(cs);
+        mma16((u & 1) ? sb : sa, cs.kf, cs.qf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      f32x4 s = sa + sb;
+      if constexpr (SHARED) {   // publish the wave's next tile's coarse angles
+        const f32x2 c = coarse_l;
+        coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
+        coarse_l[1] = c[1] * step_l[0] + c[0] * step_l[1];
+        lds_st<f32x2>(coarse_s + lane * 8, coarse_l);   // read next tile, after the fence below
+      }
+
+      // online softmax; lane holds keys 4*kg + v of head column hcol
+      float mt = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (key0 + 4 * kg + v >= cur.keys) s[v] = -INFINITY;
+        mt = fmaxf(mt, s[v]);
+      }
+      mt = max_across_kg(mt);
+      const bool rescale = __any(mt > m_run + kTau);
+      const float m_new = rescale ? fmaxf(m_run, mt) : m_run;
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      m_run = m_new;
+      Frag4<T> pf4;
+      float psum = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(s[v] - m_use);
+        psum += p;
+        frag_set(pf4, v, p);
+      }
+      if (rescale) {
+#pragma unroll
+        for (int t = 0; t < C::kDBlocks; ++t) o[t] *= alpha;
+        l_part *= alpha;
+      }
+      l_part += psum;
+
+      // O^T += V^T P^T, reads kVAhead blocks ahead
+      Frag4<T> vf[kVAhead];
+#pragma unroll
+      for (int t = 0; t < kVAhead; ++t) value_frag<C>(vf[t], v_lane + buf, t);
+#pragma unroll
+      for (int t = 0; t < C::kDBlocks; ++t) {
+        const Frag4<T> vc = vf[t % kVAhead];
+        if (t + kVAhead < C::kDBlocks) value_frag<C>(vf[t % kVAhead], v_lane + buf, t + kVAhead);
+        mma16k16(o[t], vc, pf4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      lds_fence();   // this tile's LDS reads are done before its buffer is refilled
+      issue(k + 2);
     }
 
-    // online softmax; lane holds keys 4*kg + v of head column hcol
-    float mt = -INFINITY;
+    // ---- this wave's partial result for the segment --------------------------------
+    // Slot kWaves * (wg + seg) + wave: wg + seg is distinct for every (workgroup,
+    // segment) pair that exists, as a workgroup's segments begin where the
+    // previous workgroup's end.  A wave without tiles here leaves m = -inf.
+    const float l = sum_across_kg(l_part);
+    float* slot = a.partials + static_cast<size_t>(C::kWaves * (wg + seg) + wave) * kSlot;
+    if (hcol < G) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (key0 + 4 * kg + v >= w1) s[v] = -INFINITY;
-      mt = fmaxf(mt, s[v]);
+      for (int t = 0; t < C::kDBlocks; ++t) *reinterpret_cast<f32x4*>(slot + hcol * D + 16 * t + 4 * kg) = o[t];
+      if (kg == 0) *reinterpret_cast<f32x2*>(slot + G * D + 2 * hcol) = f32x2{m_run, l};
     }
-    mt = max_across_kg(mt);
-    const bool rescale = __any(mt > m_run + kTau);
-    const float m_new = rescale ? fmaxf(m_run, mt) : m_run;
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    m_run = m_new;
-    Frag4<T> pf;
-    float psum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float p = __builtin_amdgcn_exp2f(s[v] - m_use);
-      psum += p;
-      frag_set(pf, v, p);
-    }
-    if (rescale) {
-#pragma unroll
-      for (int t = 0; t < C::kDBlocks; ++t) o[t] *= alpha;
-      l_part *= alpha;
-    }
-    l_part += psum;
-
-    // O^T += V^T P^T, reads kVAhead blocks ahead
-    Frag4<T> vf[kVAhead];
-#pragma unroll
-    for (int t = 0; t < kVAhead; ++t) value_frag<C>(vf[t], v_lane + buf, t);
-#pragma unroll
-    for (int t = 0; t < C::kDBlocks; ++t) {
-      const Frag4<T> cur = vf[t % kVAhead];
-      if (t + kVAhead < C::kDBlocks) value_frag<C>(vf[t % kVAhead], v_lane + buf, t + kVAhead);
-      mma16k16(o[t], cur, pf);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lds_fence();   // this tile's LDS reads are done before its buffer is refilled
-    if (it + 2 < ntiles) issue_tile<C>(tiles + buf, rk, rv, key0 + 2 * C::KT, nkeys, lane);
-  }
-
-  // ---- merge the waves of this item ------------------------------------------------
-  // comb: [wave][G][D] outputs | [wave][32] (m per head, l per head) | [G][kWaves]
-  // weights exp2(m_w - M) (divided by the item's sum when it is the only chunk)
-  // | [G][2] (M, L).
-  const float l = sum_across_kg(l_part);
-  __syncthreads();                                          // tiles are no longer read
-  float* comb = reinterpret_cast<float*>(smem);
-  float* ml = comb + C::kWaves * G * D;
-  float* wts = ml + C::kWaves * 32;
-  float* stats = wts + G * C::kWaves;
-  if (hcol < G) {
-    float* mine = comb + (wave * G + hcol) * D + 4 * kg;
-#pragma unroll
-    for (int t = 0; t < C::kDBlocks; ++t) *reinterpret_cast<f32x4*>(mine + 16 * t) = o[t];
-    if (kg == 0) {
-      ml[wave * 32 + hcol] = m_run;
-      ml[wave * 32 + 16 + hcol] = l;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    float M = -INFINITY;
-    for (int w = 0; w < C::kWaves; ++w) M = fmaxf(M, ml[w * 32 + h]);
-    float L = 0.f;
-    float e[C::kWaves];
-#pragma unroll
-    for (int w = 0; w < C::kWaves; ++w) {
-      const float mw = ml[w * 32 + h];
-      e[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L += e[w] * ml[w * 32 + 16 + h];
-    }
-    const float scale = (n_chunks == 1) ? 1.0f / L : 1.0f;
-#pragma unroll
-    for (int w = 0; w < C::kWaves; ++w) wts[h * C::kWaves + w] = e[w] * scale;
-    stats[2 * h] = M;
-    stats[2 * h + 1] = L;
-  }
-  __syncthreads();
-  float* part = a.partials + ((head * a.n_chunks + chunk) * G) * (D + 2);
-  for (int g4 = threadIdx.x; g4 < G * D / 4; g4 += kThreads) {
-    const int h = g4 / (D / 4), d = 4 * (g4 % (D / 4));
-    f32x4 acc = f32x4{};
-#pragma unroll
-    for (int w = 0; w < C::kWaves; ++w)
-      acc += wts[h * C::kWaves + w] * *reinterpret_cast<const f32x4*>(comb + (w * G + h) * D + d);
-    if (n_chunks == 1) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) out[h * D + d + v] = from_f32<T>(acc[v]);
-    } else {
-      float* dst = part + h * (D + 2) + 2 + d;              // 8-byte aligned
-      *reinterpret_cast<f32x2*>(dst) = f32x2{acc[0], acc[1]};
-      *reinterpret_cast<f32x2*>(dst + 2) = f32x2{acc[2], acc[3]};
-      if (d == 0) *reinterpret_cast<f32x2*>(part + h * (D + 2)) = f32x2{stats[2 * h], stats[2 * h + 1]};
-    }
+    wait_vm_le<0>();   // stores retired: later tile waits count copies only
+    if (p_end >= t_end) break;
+    do seg_next(cur, a); while (cur.n == 0);
   }
 }
 
-// Log-sum-exp merge of the chunk partials of one (sequence, query head): the
-// chunk weights exp2(m_c - M) are computed once into LDS, then each thread
-// accumulates whole head dims across chunks (consecutive threads, consecutive
-// dims).
-template <typename T, int D, int G>
+// Log-sum-exp merge of one (sequence, query head): the partials of the waves of
+// every workgroup that streamed the segment.  Their weights exp2(m_i - M) go to
+// LDS once; then each thread accumulates whole head dims (consecutive threads,
+// consecutive dims).  Invalid lengths get a NaN row.
+template <typename T, int D, int G, bool SHARED>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  using C = DecodeCfg<T, D, G, SHARED>;
+  constexpr int kSlot = G * D + 64;
   __shared__ float wgt[1024];
   __shared__ float red[256];
-  const int h = blockIdx.x % G, kvh = blockIdx.x / G, b = blockIdx.y;
-  const int nkeys = decode_keys(a, b);
-  if (nkeys < 0) return;
-  const int n_chunks = (nkeys + kDecodeChunk - 1) / kDecodeChunk;
-  if (n_chunks <= 1) return;
-  const int64_t head = static_cast<int64_t>(b) * a.n_kv_heads + kvh;
-  const float* part = a.partials + head * a.n_chunks * G * (D + 2) + h * (D + 2);
-  constexpr int kStride = G * (D + 2);          // floats between chunks
+  const int seg = blockIdx.x / G, h = blockIdx.x % G;
+  const int b = seg / a.n_kv_heads, kvh = seg % a.n_kv_heads;
   const int t = threadIdx.x;
+  T* __restrict__ out = static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G + h) * D;
+  const int keys = decode_keys(a, b);
+  if (keys < 0) {
+    for (int d = t; d < D; d += 256) out[d] = from_f32<T>(NAN);
+    return;
+  }
+  const int n = (keys + C::KT - 1) / C::KT;
+  const int t_all = a.n_kv_heads * a.tile_prefix[a.batch];
+  const int t_seg = a.n_kv_heads * a.tile_prefix[b] + kvh * n;
+  const int64_t P = a.n_wgs;
+  const int w_lo = static_cast<int>((static_cast<int64_t>(t_seg + 1) * P - 1) / t_all);
+  const int w_hi = static_cast<int>((static_cast<int64_t>(t_seg + n) * P - 1) / t_all);
+  const int count = (w_hi - w_lo + 1) * C::kWaves;    // <= kWaves * P <= 1024
+  auto slot = [&](int i) {
+    return a.partials + static_cast<size_t>(C::kWaves * (w_lo + i / C::kWaves + seg) + i % C::kWaves) * kSlot;
+  };
+  // A workgroup with an empty share (fewer tiles than workgroups) wrote nothing.
+  auto written = [&](int i) {
+    const int64_t w = w_lo + i / C::kWaves;
+    return (t_all * w) / P < (t_all * (w + 1)) / P;
+  };
 
   float mx = -INFINITY;
-  for (int c = t; c < n_chunks; c += 256) mx = fmaxf(mx, part[c * kStride]);
+  for (int i = t; i < count; i += 256)
+    if (written(i)) mx = fmaxf(mx, slot(i)[G * D + 2 * h]);
   red[t] = mx;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -552,10 +626,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const float M = red[0];
   __syncthreads();
   float lsum = 0.f;
-  for (int c = t; c < n_chunks; c += 256) {
-    const float w = __builtin_amdgcn_exp2f(part[c * kStride] - M);
-    wgt[c] = w;
-    lsum += w * part[c * kStride + 1];
+  for (int i = t; i < count; i += 256) {
+    float w = 0.f;
+    if (written(i)) {
+      const float* p = slot(i);
+      const float mi = p[G * D + 2 * h];
+      w = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - M);
+      lsum += w * p[G * D + 2 * h + 1];
+    }
+    wgt[i] = w;
   }
   red[t] = lsum;
   __syncthreads();
@@ -564,52 +643,82 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     __syncthreads();
   }
   const float inv = 1.0f / red[0];
-  T* __restrict__ out = static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G + h) * D;
   for (int d = t; d < D; d += 256) {
     float o = 0.f;
-    for (int c = 0; c < n_chunks; ++c) o += wgt[c] * part[c * kStride + 2 + d];
+    for (int i = 0; i < count; ++i)
+      if (wgt[i] != 0.f) o += wgt[i] * slot(i)[h * D + d];
     out[d] = from_f32<T>(o * inv);
   }
 }
 
 template <typename T, int D, int G, bool SHARED>
-static hipError_t launch_one(const DecodeArgs& a, int batch, hipStream_t s, LaunchTimer timer) {
+static hipError_t launch_one(const DecodeArgs& a, hipStream_t s, LaunchTimer timer) {
   using C = DecodeCfg<T, D, G, SHARED>;
   if (timer) timer(s, 2, true);
-  hipLaunchKernelGGL((decode_kernel<T, D, G, SHARED>), dim3(a.n_chunks, a.n_kv_heads, batch),
-                     dim3(C::kWaves * 64), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, SHARED>), dim3(a.n_wgs), dim3(C::kWaves * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (timer) timer(s, 2, false);
-  if (e != hipSuccess || a.n_chunks <= 1) return e;
+  if (e != hipSuccess) return e;
   if (timer) timer(s, 3, true);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(a.n_kv_heads * G, batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, G, SHARED>), dim3(a.batch * a.n_kv_heads * G), dim3(256), 0, s,
+                     a);
   e = hipGetLastError();
   if (timer) timer(s, 3, false);
   return e;
 }
 
 template <typename T, int D, bool SHARED>
-static hipError_t launch_g(const DecodeArgs& a, int group, int batch, hipStream_t s, LaunchTimer tm) {
+static hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t s, LaunchTimer tm) {
   switch (group) {
-    case 1: return launch_one<T, D, 1, SHARED>(a, batch, s, tm);
-    case 2: return launch_one<T, D, 2, SHARED>(a, batch, s, tm);
-    case 4: return launch_one<T, D, 4, SHARED>(a, batch, s, tm);
-    case 8: return launch_one<T, D, 8, SHARED>(a, batch, s, tm);
+    case 1: return launch_one<T, D, 1, SHARED>(a, s, tm);
+    case 2: return launch_one<T, D, 2, SHARED>(a, s, tm);
+    case 4: return launch_one<T, D, 4, SHARED>(a, s, tm);
+    case 8: return launch_one<T, D, 8, SHARED>(a, s, tm);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, int kv_shared,
                          int batch, hipStream_t s, LaunchTimer tm) {
-  if (dtype == 0 && head_dim == 512) return kv_shared ? launch_g<bf16, 512, true>(a, group, batch, s, tm)
-                                                      : launch_g<bf16, 512, false>(a, group, batch, s, tm);
-  if (dtype == 0 && head_dim == 256) return kv_shared ? launch_g<bf16, 256, true>(a, group, batch, s, tm)
-                                                      : launch_g<bf16, 256, false>(a, group, batch, s, tm);
-  if (dtype == 1 && head_dim == 512) return kv_shared ? launch_g<float, 512, true>(a, group, batch, s, tm)
+  (void)batch;
+  if (dtype == 0 && head_dim == 512) return kv_shared ? launch_g<bf16, 512, true>(a, group, s, tm)
+                                                      : launch_g<bf16, 512, false>(a, group, s, tm);
+  if (dtype == 0 && head_dim == 256) return kv_shared ? launch_g<bf16, 256, true>(a, group, s, tm)
+                                                      : launch_g<bf16, 256, false>(a, group, s, tm);
+  if (dtype == 1 && head_dim == 512) return kv_shared ? launch_g<float, 512, true>(a, group, s, tm)
                                                       : hipErrorInvalidValue;   // not built (host rejects it)
-  if (dtype == 1 && head_dim == 256) return kv_shared ? launch_g<float, 256, true>(a, group, batch, s, tm)
-                                                      : launch_g<float, 256, false>(a, group, batch, s, tm);
+  if (dtype == 1 && head_dim == 256) return kv_shared ? launch_g<float, 256, true>(a, group, s, tm)
+                                                      : launch_g<float, 256, false>(a, group, s, tm);
   return hipErrorInvalidValue;
+}
+
+template <typename T, int D, bool SHARED>
+static int waves_of() {
+  return DecodeCfg<T, D, 8, SHARED>::kWaves;   // independent of the group size
+}
+
+bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, int n_kv_heads,
+                 int max_tiles_per_seq, int n_cus, DecodePlan* plan) {
+  int waves = 0;
+  if (dtype == 0 && head_dim == 512) waves = kv_shared ? waves_of<bf16, 512, true>() : waves_of<bf16, 512, false>();
+  if (dtype == 0 && head_dim == 256) waves = kv_shared ? waves_of<bf16, 256, true>() : waves_of<bf16, 256, false>();
+  if (dtype == 1 && head_dim == 512) waves = kv_shared ? waves_of<float, 512, true>() : 0;
+  if (dtype == 1 && head_dim == 256) waves = kv_shared ? waves_of<float, 256, true>() : waves_of<float, 256, false>();
+  if (waves == 0) return false;
+  // One workgroup per CU (at most 1024 partials per segment in the merge), but
+  // no more workgroups than give each wave two tiles of the largest possible
+  // total.
+  const int64_t tiles_ub = static_cast<int64_t>(batch) * n_kv_heads * max_tiles_per_seq;
+  const int64_t by_work = (tiles_ub + 2 * waves - 1) / (2 * waves);
+  int64_t wgs = n_cus < 1 ? 1 : n_cus;
+  wgs = wgs > 1024 / waves ? 1024 / waves : wgs;
+  wgs = wgs > by_work ? by_work : wgs;
+  plan->waves = waves;
+  plan->n_wgs = static_cast<int>(wgs < 1 ? 1 : wgs);
+  plan->prefix_bytes = (static_cast<size_t>(batch + 1) * 4 + 255) / 256 * 256;
+  plan->slots = static_cast<size_t>(waves) * (plan->n_wgs + static_cast<size_t>(batch) * n_kv_heads);
+  plan->slot_floats = static_cast<size_t>(group) * head_dim + 64;
+  return true;
 }
 
 }  // namespace ga

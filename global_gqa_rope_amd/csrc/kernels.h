@@ -9,7 +9,7 @@
 namespace ga {
 
 constexpr int kPrepTile = 32;      // key positions per prefill tile (prep and attention)
-constexpr int kDecodeChunk = 1024; // cached positions per decode workgroup
+constexpr int kDecodeTile = 16;     // cached positions per decode tile
 
 // Prefill tiles in MFMA operand order.  A tile of kPrepTile = 32 keys is a
 // sequence of 1 KiB fragments; fragment f holds, for each of the 64 lanes of a
@@ -76,12 +76,26 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* seq_lens;
   void* out;
-  float* partials;         // [B][Hkv][n_chunks][G][D + 2] fp32
-  int n_q_heads, n_kv_heads, n_rot, window, cache_cap, max_seq_len, n_chunks;
+  int32_t* tile_prefix;    // [B + 1] tiles of the sequences before b (written by the split-K kernel)
+  float* partials;         // [slots][G * D + 64] fp32: o, then (m, l) per head
+  int batch, n_q_heads, n_kv_heads, n_rot, window, cache_cap, max_seq_len;
+  int n_wgs;               // split-K workgroups (the grid)
   float eps;
   float qk_scale_log2;
   double log2_theta;
 };
+
+// Launch shape and scratch of one decode call: n_wgs workgroups of `waves`
+// waves split the tiles evenly; `slots` partial results of slot_floats each.
+struct DecodePlan {
+  int waves, n_wgs;
+  size_t prefix_bytes;     // tile_prefix, padded to 256 bytes
+  size_t slots, slot_floats;
+  size_t bytes() const { return prefix_bytes + slots * slot_floats * 4; }
+};
+// Returns false if the configuration has no decode kernel.
+bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, int n_kv_heads,
+                 int max_tiles_per_seq, int n_cus, DecodePlan* plan);
 
 hipError_t launch_rope_table(void* table, int n_pos, int n_rot, int head_dim, double log2_theta,
                              hipStream_t s);

@@ -131,13 +131,19 @@ ga_status kv_append(const ga_layer* layer, int32_t batch,
                     const int32_t* positions, void* k_cache, void* v_cache,
                     int32_t cache_cap, void* stream);
 
-/* Bytes of scratch gemma_attn_decode needs (split-K partial results). */
+/*
+ * Bytes of scratch gemma_attn_decode needs: per-sequence tile offsets and the
+ * split-K partial results (one per wave and visited segment).  Depends on the
+ * layer, batch and max_seq_len only, never on the device.
+ */
 size_t gemma_attn_decode_workspace_size(const ga_layer* layer, int32_t batch,
                                         int32_t max_seq_len);
 
 /*
- * Decode: one query token per sequence against its cache (split-K over the
- * cached positions, then a log-sum-exp merge of the partial results).
+ * Decode: one query token per sequence against its cache.  A persistent
+ * split-K pass (one workgroup per CU, each streaming an equal share of all
+ * cached positions of all sequences and KV heads) is followed by a
+ * log-sum-exp merge of the partial results.
  *
  *   q        [B, Hq, d] raw query of the new token, at position seq_lens[b]-1
  *   q_gain   [d]
@@ -146,14 +152,14 @@ size_t gemma_attn_decode_workspace_size(const ga_layer* layer, int32_t batch,
  *   seq_lens device int32 [B]: valid keys including the new token (L_b >= 1).
  *            K=V layers read slots 0..L_b-1; windowed layers the min(L_b, W)
  *            filled ring slots.
- *   max_seq_len host bound on every seq_lens[b], sizes the launch.  A sequence
- *            with L_b < 1, L_b > max_seq_len or (K=V) L_b > cache_cap gets a NaN
- *            output row instead of reading out of bounds.
+ *   max_seq_len host bound on every seq_lens[b], sizes the workspace.  A
+ *            sequence with L_b < 1, L_b > max_seq_len or (K=V) L_b > cache_cap
+ *            gets a NaN output row instead of reading out of bounds.
  *   out      [B, Hq, d]
  *   workspace >= gemma_attn_decode_workspace_size() bytes, 256-byte aligned.
  * GA_EUNSUPPORTED if one head's cache (cache_cap * d * element size) reaches
- * 2 GiB, if max_seq_len needs more than 1024 chunks of 1024 positions, or for
- * fp32 with d = 512 and a separate V cache.
+ * 2 GiB, if B * Hkv * ceil(max_seq_len / 16) exceeds 2^31 - 1, or for fp32
+ * with d = 512 and a separate V cache.
  */
 ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch,
                             const void* q, const void* q_gain,

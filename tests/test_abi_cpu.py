@@ -98,10 +98,8 @@ def test_decode_and_append_validation(lib):
     assert dec(cap=0) == 1
     assert dec(ws=None, ws_bytes=0) == 3
     assert dec(B=0) == 0
-    need = lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 4096)
-    assert need >= 2 * 4 * 4 * 8 * 514 * 4
-    # one chunk needs no partials, so no workspace
-    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 1000) == 0
+    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 4096) == decode_ws(2, 4, 8, 512, 4096)
+    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 1000) == decode_ws(2, 4, 8, 512, 1000)
     app = lambda **kw: lib.kv_append(ctypes.byref(kw.get("layer", g)), 2, FAKE, kw.get("v", None),
                                      FAKE, kw.get("pos", FAKE), FAKE, kw.get("vc", None),
                                      kw.get("cap", 4096), None)
@@ -118,4 +116,16 @@ def test_workspace_sizes_follow_the_layout(lib):
     want = s_pad * 64 * 8 + 2 * (1 * 4 * s_pad * 512 * 2)
     assert lib.gemma_attn_prefill_workspace_size(ctypes.byref(g), 1, 32768) == want
     loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
-    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(loc), 32, 65537) == 0   # W = one chunk
+    # a windowed layer reads at most W keys, whatever max_seq_len is
+    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(loc), 32, 65537) == decode_ws(32, 16, 2, 256, 1024)
+
+
+def decode_ws(B, hkv, G, d, keys, waves=4):
+    """Decode scratch: B+1 int32 tile offsets padded to 256 B, then one fp32
+    slot of G*d outputs + 64 (max, sum) words per wave and (workgroup, segment)
+    pair: waves * (P + B*hkv) slots for the largest grid P the launch may pick,
+    P = min(1024 / waves, ceil(B * hkv * ceil(keys / 16) / (2 * waves)))."""
+    tiles = B * hkv * -(-keys // 16)
+    P = min(1024 // waves, -(-tiles // (2 * waves)))
+    prefix = -(-(B + 1) * 4 // 256) * 256
+    return prefix + waves * (P + B * hkv) * (G * d + 64) * 4
