@@ -138,18 +138,21 @@ ga_status check_caches(const ga_layer* L, const void* k_cache, const void* v_cac
 }
 
 struct PrefillLayout {
-  size_t table, ws_k, ws_vt, total;
-  int seq_pad;
+  size_t table, ws_k, ws_v, total;
+  int seq_pad, kw;
 };
 
+// Workspace: RoPE table [seq_pad][n_rot] (cos, sin) fp32, key rows
+// [B][Hkv][seq_pad][kw], value rows [B][Hkv][seq_pad][d]; each 256-byte aligned.
 PrefillLayout prefill_layout(const ga_layer* L, const Derived& dv, int batch, int seq_len) {
   PrefillLayout p;
   p.seq_pad = (seq_len + ga::kPrepTile - 1) / ga::kPrepTile * ga::kPrepTile;
-  const size_t kv = static_cast<size_t>(batch) * L->n_kv_heads * p.seq_pad * L->head_dim * dv.elem;
+  p.kw = L->kv_shared ? 2 * dv.n_rot : L->head_dim;
+  const size_t rows = static_cast<size_t>(batch) * L->n_kv_heads * p.seq_pad;
   p.table = 0;
   p.ws_k = align_up(static_cast<size_t>(p.seq_pad) * dv.n_rot * 8);
-  p.ws_vt = p.ws_k + align_up(kv);
-  p.total = p.ws_vt + align_up(kv);
+  p.ws_v = p.ws_k + align_up(rows * p.kw * dv.elem);
+  p.total = p.ws_v + align_up(rows * L->head_dim * dv.elem);
   return p;
 }
 
@@ -256,6 +259,8 @@ ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_l
   if (st != GA_OK) return st;
   if (batch < 0 || seq_len < 0) return fail(GA_EINVAL, "batch and seq_len must be >= 0");
   if (seq_len > (1 << 22)) return fail(GA_EUNSUPPORTED, "seq_len above 4M positions");
+  if (static_cast<int64_t>(seq_len + ga::kPrepTile) * layer->head_dim * dv.elem > INT32_MAX)
+    return fail(GA_EUNSUPPORTED, "seq_len %d: one head's key tiles must stay under 2 GiB", seq_len);
   if (batch == 0 || seq_len == 0) return GA_OK;
   if (!q || !k || !q_gain || !k_gain || !out) return fail(GA_EINVAL, "q, k, q_gain, k_gain and out must be non-NULL");
   if (layer->kv_shared && v) return fail(GA_EINVAL, "K=V layer: v must be NULL (keys are the values)");
@@ -275,7 +280,7 @@ ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_l
     if (st == GA_OK) {
       ga::PrepArgs pa{};
       pa.k = k; pa.v = v; pa.k_gain = k_gain; pa.rope_table = ws + lay.table;
-      pa.k_cache = k_cache; pa.v_cache = v_cache; pa.ws_k = ws + lay.ws_k; pa.ws_vt = ws + lay.ws_vt;
+      pa.k_cache = k_cache; pa.v_cache = v_cache; pa.ws_k = ws + lay.ws_k; pa.ws_v = ws + lay.ws_v; pa.kw = lay.kw;
       pa.seq_len = seq_len; pa.seq_pad = lay.seq_pad; pa.n_kv_heads = layer->n_kv_heads; pa.n_rot = dv.n_rot;
       pa.window = layer->window; pa.kv_shared = layer->kv_shared; pa.cache_cap = cache_cap; pa.eps = layer->norm_eps;
       st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "prefill prep launch");
@@ -284,12 +289,12 @@ ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_l
   if (st != GA_OK) return st;
 
   ga::PrefillArgs fa{};
-  fa.q = q; fa.q_gain = q_gain; fa.rope_table = ws + lay.table; fa.ws_k = ws + lay.ws_k; fa.ws_vt = ws + lay.ws_vt;
+  fa.q = q; fa.q_gain = q_gain; fa.rope_table = ws + lay.table; fa.ws_k = ws + lay.ws_k; fa.ws_v = ws + lay.ws_v;
   fa.out = out; fa.seq_len = seq_len; fa.seq_pad = lay.seq_pad; fa.n_q_heads = layer->n_q_heads;
   fa.n_kv_heads = layer->n_kv_heads; fa.n_rot = dv.n_rot; fa.window = layer->window; fa.eps = layer->norm_eps;
   fa.qk_scale_log2 = dv.scale * 1.4426950408889634f;
   ProfScope ps(s, 0);
-  return hip_status(ga::launch_prefill_attn(fa, layer->dtype, layer->head_dim, dv.group, batch, s),
+  return hip_status(ga::launch_prefill_attn(fa, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch, s),
                     "prefill attention launch");
 }
 

@@ -11,27 +11,17 @@ namespace ga {
 constexpr int kPrepTile = 32;      // key positions per prefill tile (prep and attention)
 constexpr int kDecodeTile = 16;     // cached positions per decode tile
 
-// Prefill tiles in MFMA operand order.  A tile of kPrepTile = 32 keys is a
-// sequence of 1 KiB fragments; fragment f holds, for each of the 64 lanes of a
-// wave, the 8 elements that lane feeds one 16x16x32 MFMA.  Inside a fragment,
-// element j of lane l sits at byte ((j * sizeof(T)) / 16) * 1024 + l * 16 +
-// (j * sizeof(T)) % 16, so every operand read is 1 KiB of consecutive LDS bytes.
-// With g = l / 16 (the lane's reduction group):
-//   key tile, fragment 2u + b (u < D/32, b < 2):
-//     lane l, element j = K~[key 16b + l%16][32u + 8g + j]
-//   value tile, fragment t (t < D/16):
-//     lane l, element j = V[key tile_key(g, j)][16t + l%16]
-//   tile_key(g, j) = 4g + j for j < 4 and 16 + 4g + (j - 4) for j >= 4: the
-//   keys a 16x16 score accumulator lane holds for its column, so P goes from
-//   the score registers into the PV operand unchanged.
-template <typename T>
-__host__ __device__ constexpr int frag_bytes() { return 64 * 8 * int(sizeof(T)); }
-template <typename T>
-__host__ __device__ inline int frag_elem_off(int lane, int j) {
-  return (j * int(sizeof(T)) / 16) * 1024 + lane * 16 + (j * int(sizeof(T))) % 16;
-}
-__host__ __device__ constexpr int tile_key(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
-
+// Prefill keys and values, as the prep pass writes them for the attention
+// kernel: row-major rows per (sequence, KV head), seq_pad = S rounded up to
+// kPrepTile positions, padded rows zero.
+//   ws_v [B][Hkv][seq_pad][d]   the value row: the normalised unrotated key on
+//                               K=V layers, the raw v otherwise
+//   ws_k [B][Hkv][seq_pad][kw]  the normalised rotated key, dims 0..kw-1:
+//                               kw = 2 n_rot (the rotated head) on K=V layers,
+//                               whose remaining key dims are the value row's;
+//                               kw = d on layers with a separate V
+// The attention kernel copies 32-row tiles of both into LDS and reads them as
+// MFMA operands there (the value operand by transposing LDS reads).
 struct PrepArgs {
   const void* k;
   const void* v;
@@ -39,9 +29,9 @@ struct PrepArgs {
   const void* rope_table;  // [seq_pad][n_rot] (cos, sin) fp32
   void* k_cache;
   void* v_cache;
-  void* ws_k;              // [B][Hkv][seq_pad/32] key tiles (rotated, normalised), operand order
-  void* ws_vt;             // [B][Hkv][seq_pad/32] value tiles, operand order
-  int seq_len, seq_pad, n_kv_heads, n_rot, window, kv_shared, cache_cap;
+  void* ws_k;              // [B][Hkv][seq_pad][kw] rotated normalised keys
+  void* ws_v;              // [B][Hkv][seq_pad][d] value rows
+  int seq_len, seq_pad, n_kv_heads, n_rot, window, kv_shared, cache_cap, kw;
   float eps;
 };
 
@@ -61,8 +51,8 @@ struct PrefillArgs {
   const void* q;
   const void* q_gain;
   const void* rope_table;
-  const void* ws_k;
-  const void* ws_vt;
+  const void* ws_k;        // see PrepArgs
+  const void* ws_v;
   void* out;
   int seq_len, seq_pad, n_q_heads, n_kv_heads, n_rot, window;
   float eps;
@@ -101,8 +91,8 @@ hipError_t launch_rope_table(void* table, int n_pos, int n_rot, int head_dim, do
                              hipStream_t s);
 hipError_t launch_prefill_prep(const PrepArgs& a, int dtype, int head_dim, int batch, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, int dtype, int head_dim, int batch, hipStream_t s);
-hipError_t launch_prefill_attn(const PrefillArgs& a, int dtype, int head_dim, int group, int batch,
-                               hipStream_t s);
+hipError_t launch_prefill_attn(const PrefillArgs& a, int dtype, int head_dim, int group, int kv_shared,
+                               int batch, hipStream_t s);
 // `timer` (optional) is called before and after each of the decode kernels:
 // (stream, 2 = split-K kernel / 3 = merge kernel, before?).
 typedef void (*LaunchTimer)(hipStream_t, int, bool);

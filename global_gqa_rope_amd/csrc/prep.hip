@@ -25,7 +25,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   constexpr int kChunks = D / 8;             // 8-element chunks per row
   constexpr int kMine = kChunks / 8;         // chunks per thread
-  __shared__ __attribute__((aligned(16))) T vtile[kPrepTile][D];
+  typedef T vec8 __attribute__((ext_vector_type(8)));
 
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t = threadIdx.x;
@@ -64,28 +64,31 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   }
 
   const int64_t head_base = (static_cast<int64_t>(b) * a.n_kv_heads + h);
+  const int64_t row = head_base * a.seq_pad + pos;          // row in ws_k / ws_v
   T* __restrict__ kc = static_cast<T*>(a.k_cache);
   T* __restrict__ vc = static_cast<T*>(a.v_cache);
+  T* __restrict__ wv = static_cast<T*>(a.ws_v) + row * D;
 
-  // K=V: the cache keeps the normalised, unrotated key; it is also the value.
+  // Value row.  K=V: the normalised, unrotated key, which is also what the
+  // cache keeps.
   if (a.kv_shared) {
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
       const int d0 = (i * 8 + c8) * 8;
+      vec8 e;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vtile[r][d0 + j] = from_f32<T>(x[i][j]);
-      if (kc && valid) {
-        T* dst = kc + (head_base * a.cache_cap + pos) * D + d0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dst[j] = from_f32<T>(x[i][j]);
-      }
+      for (int j = 0; j < 8; ++j) e[j] = from_f32<T>(x[i][j]);
+      *reinterpret_cast<vec8*>(wv + d0) = e;
+      if (kc && valid) *reinterpret_cast<vec8*>(kc + (head_base * a.cache_cap + pos) * D + d0) = e;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
       const int d0 = (i * 8 + c8) * 8;
+      vec8 e;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vtile[r][d0 + j] = valid ? v[src_row + d0 + j] : from_f32<T>(0.f);
+      for (int j = 0; j < 8; ++j) e[j] = valid ? v[src_row + d0 + j] : from_f32<T>(0.f);
+      *reinterpret_cast<vec8*>(wv + d0) = e;
     }
   }
 
@@ -104,19 +107,18 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
     }
   }
 
-  // Rotated keys into the operand-ordered key tile (padded rows zero).  The
-  // 8-element chunk c of key r is fragment 2 (c / 4) + r / 16, lane
-  // r % 16 + 16 (c % 4).
-  const int64_t tile_base = (head_base * (a.seq_pad / kPrepTile) + tile) * (kPrepTile * D);
+  // Key row: dims 0..kw-1 of the rotated normalised key.
   {
-    char* kt = reinterpret_cast<char*>(static_cast<T*>(a.ws_k) + tile_base);
+    T* __restrict__ wk = static_cast<T*>(a.ws_k) + row * a.kw;
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
-      const int c = i * 8 + c8;
-      char* frag = kt + (2 * (c >> 2) + (r >> 4)) * frag_bytes<T>();
-      const int ln = (r & 15) + 16 * (c & 3);
+      const int d0 = (i * 8 + c8) * 8;
+      if (d0 < a.kw) {
+        vec8 e;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) *reinterpret_cast<T*>(frag + frag_elem_off<T>(ln, j)) = from_f32<T>(x[i][j]);
+        for (int j = 0; j < 8; ++j) e[j] = from_f32<T>(x[i][j]);
+        *reinterpret_cast<vec8*>(wk + d0) = e;
+      }
     }
   }
 
@@ -146,23 +148,6 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
       for (int j = 0; j < 8; ++j) {
         dk[d0 + j] = from_f32<T>(x[i][j]);
         dv[d0 + j] = v[src_row + d0 + j];
-      }
-    }
-  }
-  __syncthreads();
-
-  // Values into the operand-ordered value tile: head dim d goes to fragment
-  // d / 16, lanes d % 16 + 16 g, element j holding key tile_key(g, j).
-  {
-    char* vt = reinterpret_cast<char*>(static_cast<T*>(a.ws_vt) + tile_base);
-    for (int d = t; d < D; d += 256) {
-      char* frag = vt + (d >> 4) * frag_bytes<T>();
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ln = (d & 15) + 16 * g;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<T*>(frag + frag_elem_off<T>(ln, j)) = vtile[tile_key(g, j)][d];
       }
     }
   }

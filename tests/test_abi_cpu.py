@@ -111,9 +111,10 @@ def test_decode_and_append_validation(lib):
 
 def test_workspace_sizes_follow_the_layout(lib):
     g = L()
-    # table (S_pad * 64 pairs * 8 B) + two [B,Hkv,S_pad,512] bf16 tile sets
+    # table (S_pad * 64 pairs * 8 B) + key rows [B,Hkv,S_pad,128] (the rotated
+    # head of a K=V layer) + value rows [B,Hkv,S_pad,512], bf16
     s_pad = 32768
-    want = s_pad * 64 * 8 + 2 * (1 * 4 * s_pad * 512 * 2)
+    want = s_pad * 64 * 8 + 1 * 4 * s_pad * 128 * 2 + 1 * 4 * s_pad * 512 * 2
     assert lib.gemma_attn_prefill_workspace_size(ctypes.byref(g), 1, 32768) == want
     loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
     # a windowed layer reads at most W keys, whatever max_seq_len is
