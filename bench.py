@@ -24,6 +24,30 @@ import numpy as np
 MI355X_BF16_DENSE_TFLOPS = 2500.0   # published dense bf16 MFMA peak
 MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 
+# HBM bytes per launch of each kernel from rocprofv3 --pmc FETCH_SIZE and then
+# --pmc WRITE_SIZE on this benchmark, scaled by what the same counters read for
+# a plain 256 MiB device copy (FETCH_SIZE x 2, WRITE_SIZE x 1), together with a
+# digest of the kernel's sources at the time.  Reported only while the sources
+# still match; after any change to them the figure is stale and reads null.
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
+MEASURED_TRAFFIC = {
+    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "6f052eeace417c74",
+                     "bytes": 11211247221},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "da8a4ea7f2743b77",
+                      "bytes": 4289395275},
+}
+
+
+def measured_traffic(kernel):
+    """Counter-measured HBM bytes per launch of `kernel`, or None if its sources changed since."""
+    import hashlib
+    rec = MEASURED_TRAFFIC[kernel]
+    h = hashlib.sha256()
+    for name in rec["sources"]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return rec["bytes"] if h.hexdigest()[:16] == rec["digest"] else None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -186,7 +210,8 @@ def main():
                    "batch": 1, "seq_len": 32768, "flops_per_step": pre["flops"]},
         "roofline": {"kernel": "prefill_attn_kernel<bf16,512,8>", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / MI355X_BF16_DENSE_TFLOPS, 4),
+                     "traffic": measured_traffic("prefill_attn"),
                      "avg_ms": round(pre["attn_ms"], 4), "prep_avg_ms": round(pre["prep_ms"], 4)},
     }
     if not args.no_decode:
@@ -199,7 +224,8 @@ def main():
             "kv_bytes": dec["bytes"],
             "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V>", "bound": "hbm",
                          "achieved": round(split_gbs, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
-                         "frac": round(split_gbs / MI355X_HBM_GBS, 4), "traffic": None,
+                         "frac": round(split_gbs / MI355X_HBM_GBS, 4),
+                         "traffic": measured_traffic("decode_splitk"),
                          "avg_ms": round(dec["split_ms"], 4), "merge_avg_ms": round(dec["merge_ms"], 4)},
         }
     if not args.no_cpu_baseline:
