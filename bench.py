@@ -27,26 +27,32 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 # HBM bytes per launch of each kernel from rocprofv3 --pmc FETCH_SIZE and then
 # --pmc WRITE_SIZE on this benchmark, scaled by what the same counters read for
 # a plain 256 MiB device copy (FETCH_SIZE x 2, WRITE_SIZE x 1), together with a
-# digest of the kernel's sources at the time.  Reported only while the sources
+# digest of the kernel's code (comments and layout ignored) at the time.  Reported only while the sources
 # still match; after any change to them the figure is stale and reads null.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "6f052eeace417c74",
+    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1e21162a2e58c98d",
                      "bytes": 11211247221},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "da8a4ea7f2743b77",
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2e66e576819ab91a",
                       "bytes": 4289395275},
 }
 
 
 def measured_traffic(kernel):
     """Counter-measured HBM bytes per launch of `kernel`, or None if its sources changed since."""
+    return MEASURED_TRAFFIC[kernel]["bytes"] if source_digest(kernel) == MEASURED_TRAFFIC[kernel]["digest"] else None
+
+
+def source_digest(kernel):
+    """SHA-256 prefix of the kernel's sources with // comments and whitespace removed."""
     import hashlib
-    rec = MEASURED_TRAFFIC[kernel]
+    import re
     h = hashlib.sha256()
-    for name in rec["sources"]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
-    return rec["bytes"] if h.hexdigest()[:16] == rec["digest"] else None
+    for name in MEASURED_TRAFFIC[kernel]["sources"]:
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            code = re.sub(r"//[^\n]*", "", f.read())
+        h.update(" ".join(code.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def parse():

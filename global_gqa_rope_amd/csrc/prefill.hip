@@ -25,7 +25,7 @@
 // value rows (the normalised unrotated keys) plus only the rotated head of the
 // keys (dims 0..127, p-RoPE section "p-RoPE（低频剪枝旋转位置编码）"): the
 // other key dims are read from the value rows, so a tile takes 40 KiB instead
-// of 64 and three fit in LDS.  Windowed layers start at the first tile that
+// of 64 and four fit in LDS.  Windowed layers start at the first tile that
 // can hold a visible key and mask keys with j <= i - W (section
 // "交错层（局部与全局注意力）").
 #include <type_traits>
