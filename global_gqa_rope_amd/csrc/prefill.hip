@@ -18,6 +18,14 @@
 // Each wave keeps 32 rows x d fp32 accumulators (256 registers at d = 512, in
 // the accumulation register file).
 //
+// With three or more stages (every bf16 layer) the tile loop is software
+// pipelined: step i takes the row max of tile i's scores, then runs the QK^T
+// MFMAs of tile i + 1 with tile i's exponentials under them, then the PV
+// MFMAs of tile i.  With one wave per SIMD nothing else would feed the matrix
+// unit while a wave computes its softmax.  Edge tiles (the causal diagonal,
+// the window's lower edge) run a masked copy of the step; all other tiles
+// skip the mask.
+//
 // Tiles are 32 row-major rows (16-byte chunk c of row r stored at
 // c ^ swz(r), see row_swizzle),
 // copied global -> LDS by buffer loads that write LDS directly, kStages tiles
@@ -130,14 +138,17 @@ __device__ __forceinline__ float read_acc(float a) {
 }
 
 // Scheduling pattern for a pipelined operand stream of N MFMAs, R LDS reads
-// each, whose reads run A MFMAs ahead: the first A*R reads, then one MFMA and
-// R reads alternately, then the last A MFMAs; NV global->LDS copies go one
-// after every SV-th MFMA.  Keeps the reads in flight where the scheduler would
+// each, whose reads run A MFMAs ahead: the first A*R reads (when PRE; else
+// they were issued before this region), then one MFMA and R reads
+// alternately, then the last A MFMAs; NV global->LDS copies go one after
+// every SV-th MFMA.  Keeps the reads in flight where the scheduler would
 // otherwise trade prefetch depth for registers, and spreads the copies so the
-// wave never queues many of them at once.
-template <int A, int N, int R, int NV = 0, int SV = 1>
+// wave never queues many of them at once.  Other work (the exponentials) is
+// left to the scheduler: fixed vector-ALU slots between the MFMAs measured
+// slower.
+template <int A, int N, int R, int NV = 0, int SV = 1, bool PRE = true>
 __device__ __forceinline__ void interleave_reads_mfma() {
-  __builtin_amdgcn_sched_group_barrier(0x100, A * R, 0);
+  if constexpr (PRE) __builtin_amdgcn_sched_group_barrier(0x100, A * R, 0);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -165,11 +176,13 @@ struct CopyPiece {
 };
 template <typename C>
 __device__ __forceinline__ CopyPiece copy_piece(int k, int wave, int lane) {
+  static_assert(C::kDmaK % C::kWaves == 0, "key-region instructions split evenly over the waves");
+  constexpr int kPerWaveK = C::kDmaK / C::kWaves;
   CopyPiece cp;
-  const int i = k * C::kWaves + wave;
-  cp.is_k = i < C::kDmaK;
-  const int j = cp.is_k ? i : i - C::kDmaK;                 // piece within its region
-  cp.rb = cp.is_k ? C::kKRowBytes : C::kVRowBytes;          // uniform per (k, wave)
+  cp.is_k = k < kPerWaveK;                                  // known at compile time with k
+  const int j = (cp.is_k ? k : k - kPerWaveK) * C::kWaves + wave;   // piece within its region
+  const int i = (cp.is_k ? 0 : C::kDmaK) + j;               // = k kWaves + wave
+  cp.rb = cp.is_k ? C::kKRowBytes : C::kVRowBytes;
   int r, slot;
   if (cp.rb >= 1024) {
     r = j / (cp.rb / 1024);
@@ -191,6 +204,13 @@ __device__ __forceinline__ void issue_tile(BufRsrc rk, BufRsrc rv, int tile, lds
   }
 }
 
+// off ^ x, where off is a lane's offset into a row-aligned region (row base,
+// plus a swizzled chunk in bits 4..7, plus bits below 4) and x < the row size
+// is a per-step chunk offset.  Bits 8 and up of x meet only zero bits of off
+// below the row base, so they add without carry: only the low byte needs a
+// VALU XOR, and the rest becomes the read's immediate offset.
+__device__ __forceinline__ int chunk_xor(int off, int x) { return (off ^ (x & 0xff)) + (x & ~0xff); }
+
 // QK^T A operand of step u: the 8 elements of key row l%32 at dims 16u + 8h ..,
 // at stage `st`, from the lane's row offset `off` (lane part of the chunk
 // already swizzled; the step part enters as an XOR).
@@ -199,11 +219,12 @@ __device__ __forceinline__ V st_ld(const lds_char* st, int off) {
   return *(const __attribute__((address_space(3))) V*)(st + off);
 }
 __device__ __forceinline__ void key_frag(Frag8<bf16>& f, const lds_char* st, int off, int u) {
-  f.v = st_ld<bf16x8>(st, off ^ ((2 * u) << 4));
+  f.v = st_ld<bf16x8>(st, chunk_xor(off, (2 * u) << 4));
 }
 __device__ __forceinline__ void key_frag(Frag8<float>& f, const lds_char* st, int off, int u) {
-  const f32x4 a = st_ld<f32x4>(st, off ^ ((4 * u) << 4));
-  const f32x4 b = st_ld<f32x4>(st, off ^ ((4 * u) << 4) ^ 16);
+  const int o = chunk_xor(off, (4 * u) << 4);
+  const f32x4 a = st_ld<f32x4>(st, o);
+  const f32x4 b = st_ld<f32x4>(st, o ^ 16);
   f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
   f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
 }
@@ -221,7 +242,7 @@ __device__ __forceinline__ void value_frag(Frag8<bf16>& f, const lds_char* st, c
   typedef short s16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int off = (vt[s] ^ ((4 * t) << 4)) + c * 16 * C::kVRowBytes;
+    const int off = chunk_xor(vt[s], (4 * t) << 4) + c * 16 * C::kVRowBytes;
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(st + off));
     const bf16x4 w = __builtin_bit_cast(bf16x4, v);
 #pragma unroll
@@ -294,101 +315,101 @@ struct RowState {
   float m_run, l_part;
 };
 
-// One key tile: copy tile `next_tile` into `nxt` (spread over the QK^T steps), S^T,
-// online softmax and O^T += V^T P^T from `cur`.  `cur` and `nxt` are distinct
-// stages: with them as restrict pointers the compiler knows the copy does not
-// feed this tile's reads (the kernel's own waits order the copies), and adds
-// no waits for the copies before the LDS reads.
+// ---- pieces of a tile step ----------------------------------------------------
+
+// First kKAhead key fragments of the S^T of the tile at `cur`.
 template <typename C, typename T, int D>
-__device__ __forceinline__ void tile_step(const lds_char* __restrict__ cur, lds_char* __restrict__ nxt,
-                                          const char* kbase, const char* vbase, uint32_t kspan, uint32_t vspan,
-                                          int next_tile, int wave, int lane,
-                                          const LaneOffsets& lo, const QSource<T, D>& qs, int key0, int pos, int w_first,
-                                          int window, RowState<C::kDBlocks>& rs) {
-  constexpr bool kQRegs = sizeof(T) == 2;
-  const int h = lane >> 5;
-  // Copies of tile next_tile into `nxt` go between the QK^T MFMAs, one per
-  // kDmaStride steps.  Tiles past the sequence's padded end read zeros (the
-  // buffer's range check); past this workgroup's last tile they are never used.
-  const BufRsrc rk = make_rsrc(kbase, kspan), rv = make_rsrc(vbase, vspan);
-  // The copy offsets are recomputed each tile (two VALU ops each) instead of
-  // being kept live across the loop in registers the MFMA operands need.
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
-  constexpr int kDmaStride = C::kQSteps / C::kDmaPerWave > 0 ? C::kQSteps / C::kDmaPerWave : 1;
-  static_assert(C::kDmaPerWave <= C::kQSteps, "one copy per QK^T step at most");
-  auto copy = [&](int k) {
-    const CopyPiece cp = copy_piece<C>(k, wave, ln);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.is_k ? rk : rv, nxt + cp.lds, 16, cp.voff, next_tile * C::KT * cp.rb,
-                                             0, 0);
-  };
-
-  // S^T[key][row]: reads kKAhead fragments ahead of the MFMAs
-  f32x16 s = f32x16{};
-  {
-    auto kfrag = [&](Frag8<T>& f, int u) { key_frag(f, cur, u < C::kKSteps ? lo.kq : lo.vq, u); };
-    Frag8<T> kf[C::kKAhead];
+__device__ __forceinline__ void qk_prefetch(Frag8<T> (&kf)[C::kKAhead], const lds_char* cur, const LaneOffsets& lo) {
 #pragma unroll
-    for (int u = 0; u < C::kKAhead; ++u) kfrag(kf[u], u);
+  for (int u = 0; u < C::kKAhead; ++u) key_frag(kf[u], cur, u < C::kKSteps ? lo.kq : lo.vq, u);
+}
+// S^T[key][row] of the tile at `cur` from prefetched fragments `kf`, later
+// fragments read kKAhead steps ahead of the MFMAs.  `copy(k)`, k < NC, goes
+// after every (kQSteps / NC)-th MFMA, and `work(u)` (other, independent work)
+// after MFMA u in program order.
+template <typename C, typename T, int D, int NC, typename CopyFn, typename WorkFn>
+__device__ __forceinline__ void qk_run(f32x16& s, Frag8<T> (&kf)[C::kKAhead], const lds_char* cur,
+                                       const LaneOffsets& lo, const QSource<T, D>& qs, int h, CopyFn&& copy,
+                                       WorkFn&& work) {
+  constexpr int kStride = NC > 0 ? C::kQSteps / NC : 1;
+  static_assert(NC <= C::kQSteps, "one copy per QK^T MFMA at most");
+  s = f32x16{};
 #pragma unroll
-    for (int u = 0; u < C::kQSteps; ++u) {
-      const Frag8<T> k = kf[u % C::kKAhead];
-      if (u + C::kKAhead < C::kQSteps) kfrag(kf[u % C::kKAhead], u + C::kKAhead);
-      mma32(s, k, query_frag(qs, u, h));
-      if (C::kStages > 1 && u % kDmaStride == 0 && u / kDmaStride < C::kDmaPerWave) copy(u / kDmaStride);
-    }
-    if constexpr (kQRegs) interleave_reads_mfma<C::kKAhead, C::kQSteps, 1, (C::kStages > 1 ? C::kDmaPerWave : 0), kDmaStride>();
+  for (int u = 0; u < C::kQSteps; ++u) {
+    const Frag8<T> k = kf[u % C::kKAhead];
+    if (u + C::kKAhead < C::kQSteps)
+      key_frag(kf[u % C::kKAhead], cur, u + C::kKAhead < C::kKSteps ? lo.kq : lo.vq, u + C::kKAhead);
+    mma32(s, k, query_frag(qs, u, h));
+    if (NC > 0 && u % kStride == 0 && u / kStride < NC) copy(u / kStride);
+    work(u);
   }
+  if constexpr (sizeof(T) == 2) interleave_reads_mfma<C::kKAhead, C::kQSteps, 1, NC, kStride, false>();
+}
 
-  // mask + online softmax: register r of this lane is key key0 + 8(r/4) + 4h + r%4
-  // of query row m
-  const bool need_mask = (key0 + C::KT - 1 > w_first) || (window > 0 && key0 <= w_first + C::PW - 1 - window);
-  if (need_mask) {
-    // visible keys: pos - W < key <= pos; with key = key0 + 4h + c_r,
-    // c_r = 8(r/4) + r%4, that is diff - W < c_r <= diff
-    const int diff = pos - key0 - 4 * h;
-    const int low = window > 0 ? diff - window : -(1 << 30);
+// Scores of an edge tile masked: register r of this lane is key
+// key0 + 8(r/4) + 4h + r%4 of the lane's query row; visible keys satisfy
+// pos - W < key <= pos, that is diff - W < c_r <= diff with
+// diff = pos - key0 - 4h and c_r = 8(r/4) + r%4.
+__device__ __forceinline__ void mask_scores(float (&sv)[16], int key0, int pos, int window, int h) {
+  const int diff = pos - key0 - 4 * h;
+  const int low = window > 0 ? diff - window : -(1 << 30);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c = 8 * (r / 4) + (r % 4);
-      s[r] = (c <= diff && c > low) ? s[r] : -INFINITY;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int c = 8 * (r / 4) + (r % 4);
+    sv[r] = (c <= diff && c > low) ? sv[r] : -INFINITY;
   }
-  float mt = s[0];
+}
+
+// Row max of the tile's scores and the lazy rescale of the running state: O
+// and the partial sum are rescaled only when the row max grows by more than
+// 2^kTau (scores are bounded after QKNorm, so this is rare past the first
+// tiles).  Returns the max the exponentials subtract.
+template <int NB>
+__device__ __forceinline__ float update_max(const float (&sv)[16], RowState<NB>& rs) {
+  float mt = sv[0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+  for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sv[r]);
   mt = max_halves(mt);
-  constexpr float kTau = 8.0f;   // rescale only when the running max grows by > 2^8
+  constexpr float kTau = 8.0f;
   if (__any(mt > rs.m_run + kTau)) {
     const float m_new = fmaxf(rs.m_run, mt);
     if (rs.m_run != -INFINITY) {   // nothing accumulated yet otherwise
       const float alpha = __builtin_amdgcn_exp2f(rs.m_run - m_new);
 #pragma unroll
-      for (int t = 0; t < C::kDBlocks; ++t) scale_acc(rs.o[t], alpha);
+      for (int t = 0; t < NB; ++t) scale_acc(rs.o[t], alpha);
       rs.l_part *= alpha;
     }
     rs.m_run = m_new;
   }
-  const float m_use = (rs.m_run == -INFINITY) ? 0.f : rs.m_run;
-  Frag8<T> pf[2];
+  return rs.m_run == -INFINITY ? 0.f : rs.m_run;
+}
+
+// P = exp2(S - m) into the two B operands of the PV MFMAs (score registers
+// 8c .. 8c+7 form operand c), and the lane's part of the row sum.
+template <typename T>
+__device__ __forceinline__ void tile_exps(Frag8<T> (&pf)[2], const float (&sv)[16], float m_use, float& l) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const float p = __builtin_amdgcn_exp2f(s[r] - m_use);
-    rs.l_part += p;
+    const float p = __builtin_amdgcn_exp2f(sv[r] - m_use);
+    l += p;
     frag_set(pf[r / 8], r % 8, p);
   }
+}
 
-  // O^T += V^T P^T: step f = 2t + c pairs value block t, keys 16c .. with
-  // score registers 8c .. 8c+7
-  if constexpr (kQRegs) {
+// O^T += V^T P^T from the value rows of the stage at `st`: step f = 2t + c
+// pairs value block t with keys 16c .. 16c+15 (score registers 8c .. 8c+7).
+template <typename C, typename T, int NB>
+__device__ __forceinline__ void pv_tile(const lds_char* st, const LaneOffsets& lo, const Frag8<T> (&pf)[2],
+                                        RowState<NB>& rs, int lane) {
+  if constexpr (sizeof(T) == 2) {
     Frag8<T> vf[C::kVAhead];
 #pragma unroll
-    for (int f = 0; f < C::kVAhead; ++f) value_frag<C>(vf[f], cur + C::kKBytes, lo.vt, f >> 1, f & 1);
+    for (int f = 0; f < C::kVAhead; ++f) value_frag<C>(vf[f], st + C::kKBytes, lo.vt, f >> 1, f & 1);
 #pragma unroll
     for (int f = 0; f < 2 * C::kDBlocks; ++f) {
       const Frag8<T> v = vf[f % C::kVAhead];
       if (f + C::kVAhead < 2 * C::kDBlocks)
-        value_frag<C>(vf[f % C::kVAhead], cur + C::kKBytes, lo.vt, (f + C::kVAhead) >> 1, (f + C::kVAhead) & 1);
+        value_frag<C>(vf[f % C::kVAhead], st + C::kKBytes, lo.vt, (f + C::kVAhead) >> 1, (f + C::kVAhead) & 1);
       mma32(rs.o[f >> 1], v, pf[f & 1]);
     }
     interleave_reads_mfma<C::kVAhead, 2 * C::kDBlocks, 2>();
@@ -396,10 +417,97 @@ __device__ __forceinline__ void tile_step(const lds_char* __restrict__ cur, lds_
 #pragma unroll
     for (int f = 0; f < 2 * C::kDBlocks; ++f) {
       Frag8<T> vf;
-      value_frag_f32<C>(vf, cur, f >> 1, f & 1, lane);
+      value_frag_f32<C>(vf, st, f >> 1, f & 1, lane);
       mma32(rs.o[f >> 1], vf, pf[f & 1]);
     }
   }
+}
+
+// Copy instruction k of this wave for tile `tile` into stage `nxt`.  Tiles
+// past the sequence's padded end read zeros (the buffer's range check); past
+// this workgroup's last tile they are never used.  The per-lane offsets do
+// not depend on the tile, so the compiler keeps them in registers across the
+// loop (measured faster than recomputing them at each use).
+template <typename C>
+struct TileCopier {
+  BufRsrc rk, rv;
+  lds_char* nxt;
+  int tile, wave, ln;
+  __device__ __forceinline__ void operator()(int k) const {
+    const CopyPiece cp = copy_piece<C>(k, wave, ln);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.is_k ? rk : rv, nxt + cp.lds, 16, cp.voff, tile * C::KT * cp.rb, 0, 0);
+  }
+};
+template <typename C>
+__device__ __forceinline__ TileCopier<C> make_copier(const char* kbase, const char* vbase, uint32_t kspan,
+                                                     uint32_t vspan, lds_char* nxt, int tile, int wave, int lane) {
+  return TileCopier<C>{make_rsrc(kbase, kspan), make_rsrc(vbase, vspan), nxt, tile, wave, lane};
+}
+
+// One whole tile (fewer than three stages): QK^T, softmax and PV from `cur`,
+// with the copy of tile next_tile into `nxt` spread over the QK^T MFMAs.
+// `cur` and `nxt` are distinct stages: with them as restrict pointers the
+// compiler knows the copy does not feed this tile's reads (the kernel's own
+// waits order the copies), and adds no waits for the copies before the LDS
+// reads.
+template <typename C, typename T, int D, bool MASK>
+__device__ __forceinline__ void tile_step(const lds_char* __restrict__ cur, lds_char* __restrict__ nxt,
+                                          const char* kbase, const char* vbase, uint32_t kspan, uint32_t vspan,
+                                          int next_tile, int wave, int lane, const LaneOffsets& lo,
+                                          const QSource<T, D>& qs, int key0, int pos, int window,
+                                          RowState<C::kDBlocks>& rs) {
+  const int h = lane >> 5;
+  const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, nxt, next_tile, wave, lane);
+  f32x16 s;
+  Frag8<T> kf[C::kKAhead];
+  qk_prefetch<C, T, D>(kf, cur, lo);
+  qk_run<C, T, D, (C::kStages > 1 ? C::kDmaPerWave : 0)>(s, kf, cur, lo, qs, h, copy, [](int) {});
+  float sv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sv[r] = s[r];
+  if constexpr (MASK) mask_scores(sv, key0, pos, window, h);
+  const float m_use = update_max(sv, rs);
+  Frag8<T> pf[2];
+  tile_exps(pf, sv, m_use, rs.l_part);
+  pv_tile<C, T>(cur, lo, pf, rs, lane);
+}
+
+// One pipelined step (three or more stages): the softmax and PV of tile i
+// (its scores in `s`, from the step before; its values at `vcur`), with the
+// QK^T of tile i + 1 (keys at `kcur`, scores into `s`) between the row max and
+// PV, so that the exponentials of tile i run under the QK^T MFMAs of tile
+// i + 1 instead of stalling the matrix unit.  The copy of tile next_tile into
+// `nxt` spreads over those MFMAs.  NEXT = false: the last tile, no QK^T and no
+// copy.  All three stages are distinct (restrict, as for tile_step).
+template <typename C, typename T, int D, bool MASK, bool NEXT>
+__device__ __forceinline__ void pipe_step(const lds_char* __restrict__ kcur, const lds_char* __restrict__ vcur,
+                                          lds_char* __restrict__ nxt, const char* kbase, const char* vbase,
+                                          uint32_t kspan, uint32_t vspan, int next_tile, int wave, int lane,
+                                          const LaneOffsets& lo, const QSource<T, D>& qs, int key0, int pos,
+                                          int window, RowState<C::kDBlocks>& rs, f32x16& s) {
+  const int h = lane >> 5;
+  Frag8<T> kf[C::kKAhead];
+  if constexpr (NEXT) qk_prefetch<C, T, D>(kf, kcur, lo);
+  float sv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sv[r] = s[r];
+  if constexpr (MASK) mask_scores(sv, key0, pos, window, h);
+  const float m_use = update_max(sv, rs);
+  Frag8<T> pf[2];
+  if constexpr (NEXT) {
+    // exponential r after QK^T MFMA r
+    const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, nxt, next_tile, wave, lane);
+    qk_run<C, T, D, C::kDmaPerWave>(s, kf, kcur, lo, qs, h, copy, [&](int u) {
+      if (u < 16) {
+        const float p = __builtin_amdgcn_exp2f(sv[u] - m_use);
+        rs.l_part += p;
+        frag_set(pf[u / 8], u % 8, p);
+      }
+    });
+  } else {
+    tile_exps(pf, sv, m_use, rs.l_part);
+  }
+  pv_tile<C, T>(vcur, lo, pf, rs, lane);
 }
 
 template <typename T, int D, int G, bool SHARED>
@@ -478,7 +586,6 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       lo.vt[s] = r * C::kVRowBytes + ((x ^ row_swizzle(r)) << 4) + 8 * (p & 1);
     }
   }
-  const int w_first = p0 + wave * C::PW;            // this wave's first query position
 
   RowState<C::kDBlocks> st;
 #pragma unroll
@@ -487,23 +594,80 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   st.l_part = 0.f;
   lds_char* const lds = (lds_char*)smem;
 
-  for (int kt = kt_lo; kt < kt_hi; ++kt) {
-    const int stage = (kt - kt_lo) % C::kStages;
-    // tile kt has landed once at most the later tiles' copies are in flight
-    // (every iteration copies one tile, kStages - 1 ahead)
-    wait_tiles<C>(C::kStages - 2);
-    // Tile kt visible to all waves; all waves are past tile kt - 1 (whose
-    // reads all fed MFMAs, so they have returned).  A bare barrier: the
-    // waits above already cover the copies.
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const int nstage = (kt - kt_lo + C::kStages - 1) % C::kStages;
-    tile_step<C, T, D>(lds + stage * C::kStageBytes, lds + nstage * C::kStageBytes, kbase, vbase, kspan,
-                    vspan, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos, w_first, a.window, st);
-    if (C::kStages == 1 && kt + 1 < kt_hi) {
+  // Edge tiles take the masked step: tiles [kt_lo, lo_end) reach below some
+  // row's window (key0 <= p0 + QB - 1 - W), tiles [hi_begin, kt_hi) above
+  // some row's position (key0 + KT - 1 > p0).  The tiles between are inside
+  // every row's range and skip the mask.  One loop per kind keeps a single
+  // copy of each step in the code.
+  const int lo_end = a.window > 0 ? min(kt_hi, max(kt_lo, (p0 + C::QB - 1 - a.window) / C::KT + 1)) : kt_lo;
+  const int hi_begin = max(lo_end, min(kt_hi, (p0 + 1) / C::KT));
+  auto stage_of = [&](int t) { return lds + (static_cast<unsigned>(t - kt_lo) % C::kStages) * C::kStageBytes; };
+
+  if constexpr (C::kStages >= 3) {
+    // Pipelined: step i runs the softmax and PV of tile i and the QK^T of
+    // tile i + 1.  It reads the keys of tile i + 1 and the values of tile i,
+    // and copies tile i + kStages - 1 into the stage of tile i - 1, which
+    // every wave has left once it passes the step's barrier.
+    f32x16 s;
+    {
+      wait_tiles<C>(C::kStages - 2);   // tile kt_lo landed; the next kStages - 2 may be in flight
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      issue_tile<C>(rk, rv, kt + 1, lds, wave, lane);
+      Frag8<T> kf[C::kKAhead];
+      qk_prefetch<C, T, D>(kf, stage_of(kt_lo), lo);
+      qk_run<C, T, D, 0>(s, kf, stage_of(kt_lo), lo, qs, h, [](int) {}, [](int) {});
+    }
+    auto step = [&](int kt, auto masked) {
+      // tile kt + 1 landed (one later tile may be in flight) and is visible
+      // to all waves; all waves are past step kt - 1.  A bare barrier: the
+      // wait above already covers the copies.
+      wait_tiles<C>(C::kStages - 3);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      pipe_step<C, T, D, decltype(masked)::value, true>(
+          stage_of(kt + 1), stage_of(kt), stage_of(kt + C::kStages - 1), kbase, vbase, kspan, vspan,
+          kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos, a.window, st, s);
+    };
+    const int last = kt_hi - 1;
+    const int m1 = min(lo_end, last), m2 = max(m1, min(hi_begin, last));
+    int kt = kt_lo;
+#pragma nounroll
+    for (int phase = 0; phase < 2; ++phase) {
+      const int masked_end = phase == 0 ? m1 : last;
+      for (; kt < masked_end; ++kt) step(kt, std::true_type{});
+      if (phase == 0)
+        for (; kt < m2; ++kt) step(kt, std::false_type{});
+    }
+    // The last tile (always an edge): its values landed with its keys, and
+    // nothing is copied, so neither a wait nor a barrier.
+    pipe_step<C, T, D, true, false>(stage_of(last + 1), stage_of(last), stage_of(last + C::kStages - 1), kbase,
+                                    vbase, kspan, vspan, 0, wave, lane, lo, qs, last * C::KT, pos, a.window, st, s);
+  } else {
+    // One tile per step: wait for it, barrier, then the (masked or plain) step.
+    auto run_tile = [&](int kt, auto masked) {
+      // tile kt has landed once at most the later tiles' copies are in flight
+      // (every step copies one tile, kStages - 1 ahead)
+      wait_tiles<C>(C::kStages - 2);
+      // Tile kt visible to all waves; all waves are past tile kt - 1 (whose
+      // reads all fed MFMAs, so they have returned).
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      tile_step<C, T, D, decltype(masked)::value>(stage_of(kt), stage_of(kt + C::kStages - 1), kbase, vbase, kspan,
+                                                  vspan, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos,
+                                                  a.window, st);
+      if (C::kStages == 1 && kt + 1 < kt_hi) {
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_tile<C>(rk, rv, kt + 1, lds, wave, lane);
+      }
+    };
+    int kt = kt_lo;
+#pragma nounroll
+    for (int phase = 0; phase < 2; ++phase) {
+      const int masked_end = phase == 0 ? lo_end : kt_hi;
+      for (; kt < masked_end; ++kt) run_tile(kt, std::true_type{});
+      if (phase == 0)
+        for (; kt < hi_begin; ++kt) run_tile(kt, std::false_type{});
     }
   }
 
