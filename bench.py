@@ -6,8 +6,11 @@ the host as a reported baseline.
 
 Prints one JSON line.  A step is one pass of the hot path over the workload:
 one gemma_attn_prefill call (RoPE table + key/value prep + attention) on the
-32K global-layer prefill.  The decode measurement (one gemma_attn_decode call
-on 16 sequences with lengths drawn from [4096, 131072]) is reported beside it.
+32K global-layer prefill.  Reported beside it: the global decode (one
+gemma_attn_decode call on 16 sequences with lengths drawn from [4096, 131072],
+and kv_append on its own), the local-layer prefill (B=4, S=32K, window 1024)
+and one decode step of a 6-layer stack (5 local + 1 global layer, B=32, 64K
+context, kv_append then decode per layer).
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 """
 
@@ -63,6 +66,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-local", action="store_true", help="skip the local-layer prefill leg")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 6-layer stack decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
@@ -139,11 +144,114 @@ def bench_decode(args, torch, api, W):
     split_ms, n_split = api.profile_read("decode_splitk")
     merge_ms, n_merge = api.profile_read("decode_merge")
     api.profile_reset()
+    # kv_append of the step's new token, timed on its own
+    kn = W.normal((B, shape.n_kv_heads, D), wl.seed, "k_new", torch.bfloat16, dev)
+    g_k = W.gains(D, wl.seed, "g_k", False, torch.bfloat16, dev)
+    pos = (lens - 1).to(dev)
+    api.profile_enable(True)
+    for _ in range(steps):
+        api.kv_append(lay, kn, None, g_k, pos, kc, None)
+    torch.cuda.synchronize()
+    api.profile_enable(False)
+    append_ms, n_append = api.profile_read("kv_append")
+    api.profile_reset()
     nbytes = wl.kv_bytes(lens)
     del kc
     torch.cuda.empty_cache()
     return {"sec": sec, "bytes": nbytes, "split_ms": split_ms / max(n_split, 1),
-            "merge_ms": merge_ms / max(n_merge, 1), "lens": lens}
+            "merge_ms": merge_ms / max(n_merge, 1), "append_ms": append_ms / max(n_append, 1), "lens": lens}
+
+
+def bench_local_prefill(args, torch, api, W):
+    """Local (sliding-window) layer prefill: B=4, S=32K, 32q/16kv, d=256, W=1024."""
+    wl = W.CONFIGS["local_prefill_32k"]
+    shape, S, B = wl.layer, wl.seq_len, wl.batch
+    dev = torch.device("cuda", 0)
+    x = wl.draw(dev)
+    lay = api.Layer.from_shape(shape, torch.bfloat16)
+    kc = torch.empty((B, shape.n_kv_heads, shape.window, shape.head_dim), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    out = torch.empty_like(x["q"])
+    ws = api.workspace(api.gemma_attn_prefill_workspace_size(lay, B, S), dev)
+
+    def step():
+        api.gemma_attn_prefill(lay, x["q"], x["k"], x["v"], x["g_q"], x["g_k"], kc, vc, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    sec = timed(step, args.steps, 0, torch)
+    api.profile_enable(False)
+    attn_ms, n_attn = api.profile_read("prefill_attn")
+    api.profile_reset()
+    flops = wl.flops()
+    attn_ms /= max(n_attn, 1)
+    del x, kc, vc, out, ws
+    torch.cuda.empty_cache()
+    attn = flops / (attn_ms * 1e-3) / 1e12
+    return {
+        "workload": "local layer prefill: B=4, S=32768, 32 query heads / 16 KV heads, d=256, window 1024, "
+                    "RoPE theta=1e4, QKNorm",
+        "value": round(flops / sec / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(sec * 1e3, 3),
+        "flops_per_step": flops,
+        "roofline": {"kernel": "prefill_attn_kernel<bf16,256,2>", "bound": "mfma", "achieved": round(attn, 2),
+                     "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn / MI355X_BF16_DENSE_TFLOPS, 4), "avg_ms": round(attn_ms, 4)},
+    }
+
+
+def bench_stack_decode(args, torch, api, W):
+    """One decode step of a 6-layer stack (5 local + 1 global), each layer kv_append then decode."""
+    wl_l, wl_g = W.CONFIGS["stack_decode_local"], W.CONFIGS["stack_decode_global"]
+    dev = torch.device("cuda", 0)
+    B = wl_l.batch
+    layers = []
+    for i, wl in enumerate([wl_l] * 5 + [wl_g]):
+        shape = wl.layer
+        D, Hkv = shape.head_dim, shape.n_kv_heads
+        seed = wl.seed + i
+        cap = wl.cache_cap()
+        kc = W.normal((B, Hkv, cap, D), seed, "k_cache", torch.bfloat16, dev)
+        vc = None if shape.kv_shared else W.normal((B, Hkv, cap, D), seed, "v_cache", torch.bfloat16, dev)
+        lens = wl.lengths()
+        lay = api.Layer.from_shape(shape, torch.bfloat16)
+        layers.append({
+            "lay": lay, "kc": kc, "vc": vc, "seq": lens.to(dev), "pos": (lens - 1).to(dev), "max": int(lens.max()),
+            "q": W.normal((B, shape.n_q_heads, D), seed, "q_dec", torch.bfloat16, dev),
+            "kn": W.normal((B, Hkv, D), seed, "k_new", torch.bfloat16, dev),
+            "vn": None if shape.kv_shared else W.normal((B, Hkv, D), seed, "v_new", torch.bfloat16, dev),
+            "g_q": W.gains(D, seed, "g_q", False, torch.bfloat16, dev),
+            "g_k": W.gains(D, seed, "g_k", False, torch.bfloat16, dev),
+            "out": torch.empty((B, shape.n_q_heads, D), dtype=torch.bfloat16, device=dev),
+            "ws": api.workspace(api.gemma_attn_decode_workspace_size(lay, B, int(lens.max())), dev),
+            "bytes": wl.kv_bytes(lens),
+        })
+
+    def step():
+        for L in layers:
+            api.kv_append(L["lay"], L["kn"], L["vn"], L["g_k"], L["pos"], L["kc"], L["vc"])
+            api.gemma_attn_decode(L["lay"], L["q"], L["g_q"], L["kc"], L["vc"], L["seq"], L["max"], L["out"],
+                                  L["ws"])
+
+    steps = max(args.decode_steps // 2, 8)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sec = timed(step, steps, 0, torch)
+    nbytes = sum(L["bytes"] for L in layers)
+    del layers
+    torch.cuda.empty_cache()
+    gbs = nbytes / sec / 1e9
+    return {
+        "workload": "6-layer decode step: 5 local (32q/16kv, d=256, W=1024) + 1 global K=V (32q/4kv, d=512), "
+                    "B=32, context 65536, kv_append then decode per layer",
+        "ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(B / sec, 1), "kv_bytes": nbytes,
+        "value": round(gbs, 1), "unit": "GB/s", "steps": steps,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / MI355X_HBM_GBS, 4)},
+    }
 
 
 def cpu_baseline(pre, budget_s, torch):
@@ -233,7 +341,12 @@ def main():
                          "frac": round(split_gbs / MI355X_HBM_GBS, 4),
                          "traffic": measured_traffic("decode_splitk"),
                          "avg_ms": round(dec["split_ms"], 4), "merge_avg_ms": round(dec["merge_ms"], 4)},
+            "kv_append_avg_ms": round(dec["append_ms"], 4),
         }
+    if not args.no_local:
+        line["local_prefill"] = bench_local_prefill(args, torch, api, W)
+    if not args.no_stack:
+        line["stack_decode"] = bench_stack_decode(args, torch, api, W)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds, torch)
     print(json.dumps(line), flush=True)

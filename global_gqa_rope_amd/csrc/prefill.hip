@@ -131,6 +131,11 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
                  : "v"(alpha));
   }
 }
+// Two floats as a pair of bf16 (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<bf16>(lo))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<bf16>(hi))) << 16);
+}
 __device__ __forceinline__ float read_acc(float a) {
   float v;
   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
@@ -671,18 +676,50 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- epilogue: register r of block t is dim 32t + 8(r/4) + 4h + r%4 -------------
+  // ---- epilogue: register r of block t is dim 32t + 8(r/4) + 4h + r%4 of row m -------
   wait_vm_le<0>();   // copies of tiles past the last one have landed before the workgroup ends
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last PV MFMA retired
   const float l = sum_halves(st.l_part);
-  if (!row_valid) return;
   const float inv = 1.0f / l;
   T* __restrict__ out = static_cast<T*>(a.out) +
-      ((static_cast<int64_t>(b) * a.seq_len + pos) * a.n_q_heads + qh) * D + 4 * h;
+      ((static_cast<int64_t>(b) * a.seq_len + (row_valid ? pos : 0)) * a.n_q_heads + qh) * D;
+  if constexpr (sizeof(T) == 2) {
+    // Lanes m and m + 32 hold the two 4-dim halves of each 8-dim run of row
+    // m.  One row swap per pair of runs hands each lane a whole run (lane m
+    // the even run, lane m + 32 the odd one), so every store is 16 bytes.
 #pragma unroll
-  for (int t = 0; t < C::kDBlocks; ++t)
+    for (int t = 0; t < C::kDBlocks; ++t) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[32 * t + 8 * (r / 4) + (r % 4)] = from_f32<T>(read_acc(st.o[t][r]) * inv);
+      for (int j = 0; j < 2; ++j) {
+        uint32_t lo[2], hi[2];   // runs 2j (registers 8j..8j+3) and 2j+1 (8j+4..8j+7)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          lo[e] = pack_bf16x2(read_acc(st.o[t][8 * j + 2 * e]) * inv, read_acc(st.o[t][8 * j + 2 * e + 1]) * inv);
+          hi[e] = pack_bf16x2(read_acc(st.o[t][8 * j + 4 + 2 * e]) * inv,
+                              read_acc(st.o[t][8 * j + 4 + 2 * e + 1]) * inv);
+          const auto r = __builtin_amdgcn_permlane32_swap(lo[e], hi[e], false, false);
+          lo[e] = r[0];
+          hi[e] = r[1];
+        }
+        if (row_valid)
+          *reinterpret_cast<uint4*>(out + 32 * t + 16 * j + 8 * h) = uint4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+  } else {
+    // fp32: each 4-dim half is 16 bytes already
+    if (!row_valid) return;
+#pragma unroll
+    for (int t = 0; t < C::kDBlocks; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 v;
+        v.x = read_acc(st.o[t][4 * q]) * inv;
+        v.y = read_acc(st.o[t][4 * q + 1]) * inv;
+        v.z = read_acc(st.o[t][4 * q + 2]) * inv;
+        v.w = read_acc(st.o[t][4 * q + 3]) * inv;
+        *reinterpret_cast<float4*>(out + 32 * t + 8 * q + 4 * h) = v;
+      }
+  }
 }
 
 template <typename T, int D, int G, bool SHARED>

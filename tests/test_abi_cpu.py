@@ -45,9 +45,10 @@ def L(hq=32, hkv=4, d=512, window=0, shared=1, theta=1e6, p=0.25, eps=1e-6, dtyp
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
-def prefill(lib, layer, B=1, S=16, v=None, k_cache=None, v_cache=None, cap=0, ws=FAKE, ws_bytes=1 << 40):
+def prefill(lib, layer, B=1, S=16, v=None, k_cache=None, v_cache=None, cap=0, ws=FAKE, ws_bytes=1 << 40,
+            out=FAKE):
     return lib.gemma_attn_prefill(ctypes.byref(layer), B, S, FAKE, FAKE, v, FAKE, FAKE, k_cache,
-                                  v_cache, cap, FAKE, ws, ws_bytes, None)
+                                  v_cache, cap, out, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("layer,status,msg", [
@@ -83,6 +84,8 @@ def test_prefill_argument_validation(lib):
     assert need > 0
     assert prefill(lib, g, ws_bytes=need - 1) == 3
     assert prefill(lib, g, ws=ctypes.c_void_p(0x1001)) == 1  # alignment
+    assert prefill(lib, g, out=ctypes.c_void_p(0x1008)) == 1  # rows move in 16-byte pieces
+    assert "16-byte aligned" in lib.gemma_attn_last_error().decode()
     assert prefill(lib, g, B=-1) == 1
     assert prefill(lib, g, B=0) == 0 and prefill(lib, g, S=0) == 0   # no-ops, no launch
 
