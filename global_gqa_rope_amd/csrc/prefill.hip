@@ -573,8 +573,45 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   }
   QSource<T, D> qs{qf, qrow, gq, qtable, rs, a.n_rot};
   if constexpr (kQRegs) {
+    // Gain and rotation of the register fragments.  The gains and (cos, sin)
+    // pairs of kBatch steps are all loaded before any is used, so their round
+    // trips overlap instead of queuing one after another behind the tile
+    // copies in flight.  Pair p of the row sits at table[p]; reads for
+    // p >= n_rot fall on later rows or the key rows after the table, inside
+    // the workspace, and are not used.
+    constexpr int kBatch = 4;
+    constexpr int kRotSteps = SHARED ? 8 : C::kQSteps;   // K=V layers rotate pairs 0..63, dims 0..127
 #pragma unroll
-    for (int u = 0; u < C::kQSteps; ++u) make_qfrag(qf[u], qs, u, h);
+    for (int u0 = 0; u0 < C::kQSteps; u0 += kBatch) {
+      Frag8<T> g[kBatch];
+      f32x2 cs[kBatch][4];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) load_frag(g[i], gq + 16 * (u0 + i) + 8 * h);
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (u0 + i < kRotSteps)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cs[i][j] = qtable[8 * (u0 + i) + 4 * h + j];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int u = u0 + i;
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = to_f32(qf[u].v[j]) * rs * to_f32(g[i].v[j]);
+        if (u < kRotSteps) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float r0 = x[2 * j], r1 = x[2 * j + 1];
+            rotate_pair(r0, r1, cs[i][j]);
+            const bool on = 8 * u + 4 * h + j < a.n_rot;
+            x[2 * j] = on ? r0 : x[2 * j];
+            x[2 * j + 1] = on ? r1 : x[2 * j + 1];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) frag_set(qf[u], j, x[j]);
+      }
+    }
   }
 
   // ---- lane operand offsets within a stage --------------------------------------
