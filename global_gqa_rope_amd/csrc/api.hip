@@ -265,9 +265,11 @@ ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_l
   if (!q || !k || !q_gain || !k_gain || !out) return fail(GA_EINVAL, "q, k, q_gain, k_gain and out must be non-NULL");
   if (layer->kv_shared && v) return fail(GA_EINVAL, "K=V layer: v must be NULL (keys are the values)");
   if (!layer->kv_shared && !v) return fail(GA_EINVAL, "layer with a separate V needs v");
-  // the kernels move q, k, v and out rows in 16-byte pieces
-  for (const void* t : {q, k, v, static_cast<const void*>(out)})
-    if (reinterpret_cast<uintptr_t>(t) % 16) return fail(GA_EINVAL, "q, k, v and out must be 16-byte aligned");
+  // the kernels move rows, gains and cache rows in 16-byte pieces
+  for (const void* t : {q, k, v, q_gain, k_gain, static_cast<const void*>(k_cache), static_cast<const void*>(v_cache),
+                        static_cast<const void*>(out)})
+    if (reinterpret_cast<uintptr_t>(t) % 16)
+      return fail(GA_EINVAL, "q, k, v, the gains, the caches and out must be 16-byte aligned");
   st = check_caches(layer, k_cache, v_cache, cache_cap, true, seq_len);
   if (st != GA_OK) return st;
   const PrefillLayout lay = prefill_layout(layer, dv, batch, seq_len);

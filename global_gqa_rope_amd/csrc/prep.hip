@@ -20,7 +20,8 @@ __global__ void rope_table_kernel(f32x2* __restrict__ table, int n_pos, int n_ro
 // One workgroup per (tile of kPrepTile key positions, kv head, batch).
 // Thread t owns key row r = t / 8 of the tile and the 8-element chunks
 // i * 8 + t % 8 of that row, so eight neighbouring lanes cover 64 contiguous
-// elements of one row.
+// elements of one row.  Every global access is a 16-byte vector, and all
+// loads of a thread are issued before the first use.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   constexpr int kChunks = D / 8;             // 8-element chunks per row
@@ -35,33 +36,50 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   // padding positions read the last real row (then zeroed) so no load leaves the tensor
   const int src_pos = valid ? pos : a.seq_len - 1;
   const int64_t src_row = ((static_cast<int64_t>(b) * a.seq_len + src_pos) * a.n_kv_heads + h) * D;
+  const bool has_v = !a.kv_shared;
 
   const T* __restrict__ k = static_cast<const T*>(a.k);
   const T* __restrict__ v = static_cast<const T*>(a.v);
   const T* __restrict__ gk = static_cast<const T*>(a.k_gain);
+  const f32x2* __restrict__ table = static_cast<const f32x2*>(a.rope_table) + static_cast<int64_t>(pos) * a.n_rot;
 
-  float x[kMine][8];
+  vec8 kin[kMine], vin[kMine], gin[kMine];
+  f32x2 cs[kMine][4];
 #pragma unroll
   for (int i = 0; i < kMine; ++i) {
     const int d0 = (i * 8 + c8) * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[i][j] = valid ? to_f32(k[src_row + d0 + j]) : 0.f;
+    kin[i] = *reinterpret_cast<const vec8*>(k + src_row + d0);
+    gin[i] = *reinterpret_cast<const vec8*>(gk + d0);
+    if (has_v) vin[i] = *reinterpret_cast<const vec8*>(v + src_row + d0);
   }
+  // (cos, sin) of the chunk's four pairs; pairs >= n_rot read a clamped entry
+  // of the same row and are not used
+  if (a.n_rot > 0) {
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int d0 = (i * 8 + c8) * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cs[i][j] = table[min(d0 / 2 + j, a.n_rot - 1)];
+    }
+  }
+
+  float x[kMine][8];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kMine; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ss += x[i][j] * x[i][j];
+    for (int j = 0; j < 8; ++j) {
+      x[i][j] = valid ? to_f32(kin[i][j]) : 0.f;
+      ss += x[i][j] * x[i][j];
+    }
   ss += wave_xor(ss, 1);
   ss += wave_xor(ss, 2);
   ss += wave_xor(ss, 4);
   const float rstd = 1.0f / sqrtf(ss / D + a.eps);
 #pragma unroll
-  for (int i = 0; i < kMine; ++i) {
-    const int d0 = (i * 8 + c8) * 8;
+  for (int i = 0; i < kMine; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[i][j] = x[i][j] * rstd * to_f32(gk[d0 + j]);
-  }
+    for (int j = 0; j < 8; ++j) x[i][j] = x[i][j] * rstd * to_f32(gin[i][j]);
 
   const int64_t head_base = (static_cast<int64_t>(b) * a.n_kv_heads + h);
   const int64_t row = head_base * a.seq_pad + pos;          // row in ws_k / ws_v
@@ -70,42 +88,36 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   T* __restrict__ wv = static_cast<T*>(a.ws_v) + row * D;
 
   // Value row.  K=V: the normalised, unrotated key, which is also what the
-  // cache keeps.
-  if (a.kv_shared) {
-#pragma unroll
-    for (int i = 0; i < kMine; ++i) {
-      const int d0 = (i * 8 + c8) * 8;
-      vec8 e;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = from_f32<T>(x[i][j]);
-      *reinterpret_cast<vec8*>(wv + d0) = e;
-      if (kc && valid) *reinterpret_cast<vec8*>(kc + (head_base * a.cache_cap + pos) * D + d0) = e;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kMine; ++i) {
-      const int d0 = (i * 8 + c8) * 8;
-      vec8 e;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = valid ? v[src_row + d0 + j] : from_f32<T>(0.f);
-      *reinterpret_cast<vec8*>(wv + d0) = e;
-    }
-  }
-
-  // Rotate the first 2*n_rot dims.
-  const f32x2* __restrict__ table = static_cast<const f32x2*>(a.rope_table);
+  // cache keeps.  Otherwise the raw v (zeros past the sequence).
+  vec8 vout[kMine];
 #pragma unroll
   for (int i = 0; i < kMine; ++i) {
     const int d0 = (i * 8 + c8) * 8;
-    if (d0 < 2 * a.n_rot && valid) {
+    if (has_v) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pair = d0 / 2 + j;
-        if (pair < a.n_rot)
-          rotate_pair(x[i][2 * j], x[i][2 * j + 1], table[static_cast<int64_t>(pos) * a.n_rot + pair]);
-      }
+      for (int j = 0; j < 8; ++j) vout[i][j] = valid ? vin[i][j] : from_f32<T>(0.f);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vout[i][j] = from_f32<T>(x[i][j]);
+      if (kc && valid) *reinterpret_cast<vec8*>(kc + (head_base * a.cache_cap + pos) * D + d0) = vout[i];
+    }
+    *reinterpret_cast<vec8*>(wv + d0) = vout[i];
+  }
+
+  // Rotate the first 2*n_rot dims.
+#pragma unroll
+  for (int i = 0; i < kMine; ++i) {
+    const int d0 = (i * 8 + c8) * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (d0 / 2 + j < a.n_rot) rotate_pair(x[i][2 * j], x[i][2 * j + 1], cs[i][j]);
     }
   }
+  vec8 kout[kMine];
+#pragma unroll
+  for (int i = 0; i < kMine; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kout[i][j] = from_f32<T>(x[i][j]);
 
   // Key row: dims 0..kw-1 of the rotated normalised key.
   {
@@ -113,42 +125,22 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
       const int d0 = (i * 8 + c8) * 8;
-      if (d0 < a.kw) {
-        vec8 e;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = from_f32<T>(x[i][j]);
-        *reinterpret_cast<vec8*>(wk + d0) = e;
-      }
+      if (d0 < a.kw) *reinterpret_cast<vec8*>(wk + d0) = kout[i];
     }
   }
 
-  // Windowed layers: the ring keeps the last W positions, keys rotated.
-  if (!a.kv_shared && a.window > 0 && kc && valid && pos >= a.seq_len - a.window) {
-    const int slot = pos % a.cache_cap;
+  // Separate-V layers: windowed ones keep the last W positions in a ring of
+  // cache_cap = W slots, global ones every position (slot = position); keys
+  // rotated.
+  if (has_v && kc && valid && (a.window == 0 || pos >= a.seq_len - a.window)) {
+    const int slot = a.window > 0 ? pos % a.cache_cap : pos;
     T* dk = kc + (head_base * a.cache_cap + slot) * D;
     T* dv = vc + (head_base * a.cache_cap + slot) * D;
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
       const int d0 = (i * 8 + c8) * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        dk[d0 + j] = from_f32<T>(x[i][j]);
-        dv[d0 + j] = v[src_row + d0 + j];
-      }
-    }
-  }
-  // Global layers with a separate V: slot = position.
-  if (!a.kv_shared && a.window == 0 && kc && valid) {
-    T* dk = kc + (head_base * a.cache_cap + pos) * D;
-    T* dv = vc + (head_base * a.cache_cap + pos) * D;
-#pragma unroll
-    for (int i = 0; i < kMine; ++i) {
-      const int d0 = (i * 8 + c8) * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        dk[d0 + j] = from_f32<T>(x[i][j]);
-        dv[d0 + j] = v[src_row + d0 + j];
-      }
+      *reinterpret_cast<vec8*>(dk + d0) = kout[i];
+      *reinterpret_cast<vec8*>(dv + d0) = vin[i];
     }
   }
 }

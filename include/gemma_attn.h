@@ -102,8 +102,8 @@ size_t gemma_attn_prefill_workspace_size(const ga_layer* layer, int32_t batch,
  *           the normalised rotated keys of positions max(0, S-W)..S-1.
  *   v_cache like k_cache; windowed separate-V layers only (else NULL); gets v.
  *   out     [B, S, Hq, d]
- *   q, k, v and out are read and written in 16-byte pieces and must be
- *   16-byte aligned (GA_EINVAL otherwise).
+ *   q, k, v, the gains, the caches and out are read and written in 16-byte
+ *   pieces and must be 16-byte aligned (GA_EINVAL otherwise).
  *   workspace  >= gemma_attn_prefill_workspace_size() bytes, 256-byte aligned.
  * Errors: GA_EINVAL / GA_EUNSUPPORTED / GA_EWORKSPACE before any launch,
  * GA_EHIP if a launch fails.  seq_len = 0 or batch = 0 is a no-op (GA_OK).
