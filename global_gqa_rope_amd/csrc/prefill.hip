@@ -78,6 +78,10 @@ struct PrefillCfg {
   static_assert(kStages <= 4 && (kStages - 2) * kDmaPerWave < 64, "copy counter range");
 };
 
+// Accelerator complex dies (each with its own L2) that workgroups are dealt
+// to in turn.
+constexpr int kXcds = 8;
+
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 
@@ -521,8 +525,29 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(4096))) char smem[C::kLdsBytes];
 
   const int n_qb = (a.seq_len + C::QB - 1) / C::QB;
-  const int qb = n_qb - 1 - static_cast<int>(blockIdx.x);   // longest causal rows first
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  int qb, kvh, b;
+  if (a.window > 0) {
+    // Windowed layers: every workgroup has about the same work, and the
+    // windows of neighbouring query blocks share all but two key tiles.
+    // Workgroups are dispatched round-robin over the XCDs (each with its own
+    // L2), so the linear workgroup index is remapped to give each XCD a
+    // contiguous run of (head, query block): the blocks an XCD runs together
+    // are neighbours, and their tiles are read from its L2.
+    const int n = static_cast<int>(gridDim.x * gridDim.y * gridDim.z);
+    const int w = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int per = n / kXcds, extra = n % kXcds;
+    const int x = w % kXcds, i = w / kXcds;
+    const int lin = x * per + min(x, extra) + i;              // a bijection of [0, n)
+    qb = lin % n_qb;
+    kvh = (lin / n_qb) % a.n_kv_heads;
+    b = lin / (n_qb * a.n_kv_heads);
+  } else {
+    // Causal layers: longest rows first; the round-robin dispatch spreads
+    // every length over all XCDs.
+    qb = n_qb - 1 - static_cast<int>(blockIdx.x);
+    kvh = blockIdx.y;
+    b = blockIdx.z;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, h = lane >> 5;                     // row of this lane, half of the slice
