@@ -34,8 +34,10 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 # still match; after any change to them the figure is stale and reads null.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1e21162a2e58c98d",
-                     "bytes": 11211247221},
+    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "162d930e93df2ec2",
+                     "bytes": 23110933109},
+    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "162d930e93df2ec2",
+                           "bytes": 8591068586},
     "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2e66e576819ab91a",
                       "bytes": 4289395275},
 }
@@ -198,7 +200,8 @@ def bench_local_prefill(args, torch, api, W):
         "flops_per_step": flops,
         "roofline": {"kernel": "prefill_attn_kernel<bf16,256,2>", "bound": "mfma", "achieved": round(attn, 2),
                      "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn / MI355X_BF16_DENSE_TFLOPS, 4), "avg_ms": round(attn_ms, 4)},
+                     "frac": round(attn / MI355X_BF16_DENSE_TFLOPS, 4),
+                     "traffic": measured_traffic("local_prefill_attn"), "avg_ms": round(attn_ms, 4)},
     }
 
 
