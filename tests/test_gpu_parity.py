@@ -89,6 +89,8 @@ PREFILL_CASES = [
     ("local_W64_S300", W.replace(W.LOCAL_LAYER, window=64), 1, 300),
     ("global_G4", W.replace(W.GLOBAL_LAYER, n_q_heads=16), 1, 200),
     ("local_G1_W100", W.replace(W.LOCAL_LAYER, n_q_heads=16, window=100), 1, 257),
+    # 12 workgroups: the XCD-aware order of windowed layers with a grid that 8 does not divide
+    ("local_Hkv3_W64", W.replace(W.LOCAL_LAYER, n_q_heads=6, n_kv_heads=3, window=64), 1, 200),
 ]
 
 
