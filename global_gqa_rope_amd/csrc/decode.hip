@@ -116,12 +116,12 @@ __device__ __forceinline__ int row_chunk(int r, int c) { return c ^ (r & 15); }
 // places there.  Rows past the sequence read its last row (their scores are
 // masked); the buffer's range check backs this up.
 template <typename C>
-__device__ __forceinline__ void issue_tile(uint32_t dst, BufRsrc rk, BufRsrc rv, int key0, int nkeys, int lane) {
+__device__ __forceinline__ void issue_tile(lds_char* dst, BufRsrc rk, BufRsrc rv, int key0, int nkeys, int lane) {
 #pragma unroll
   for (int i = 0; i < C::kDmaPerTile; ++i) {
     const int ik = i % C::kKDma;                   // 1 KiB piece within the K (or V) tile
     const BufRsrc& rs = (i < C::kKDma) ? rk : rv;
-    lds_char* slot = (lds_char*)(static_cast<uintptr_t>(dst + i * 1024));
+    lds_char* slot = dst + i * 1024;
     if constexpr (C::kRowBytes >= 1024) {          // piece inside one row: the key is wave-uniform
       constexpr int kPiecesPerRow = C::kRowBytes / 1024;
       const int r = ik / kPiecesPerRow;
@@ -157,14 +157,17 @@ __device__ __forceinline__ void key_frag(Frag8<float>& f, uint32_t a, int u) {
 // element i%4 of the 8-byte pieces addressed by lanes i/4 + 4j); lane l
 // addresses key 4(l/16) + (l%16)/4, dims 16t + 4(l%4) .. +3, whose chunk is
 // 2t + (l%4)/2.  fp32: four plain reads (rows 4(l/16) + j, dim 16t + l%16).
+// `buf` is the tile buffer, `off` the lane's offset in it (buffers are aligned
+// to their size, so the XOR stays inside the offset).
 template <typename C>
-__device__ __forceinline__ void value_frag(Frag4<bf16>& f, uint32_t a, int t) {
+__device__ __forceinline__ void value_frag(Frag4<bf16>& f, const lds_char* buf, uint32_t off, int t) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(static_cast<uintptr_t>(a ^ ((2 * t) << 4))));
+      (__attribute__((address_space(3))) s16x4*)(buf + (off ^ ((2 * t) << 4))));
   f.v = __builtin_bit_cast(bf16x4, v);
 }
 template <typename C>
-__device__ __forceinline__ void value_frag(Frag4<float>& f, uint32_t vtile, int t) {
+__device__ __forceinline__ void value_frag(Frag4<float>& f, const lds_char* buf, uint32_t off, int t) {
+  const uint32_t vtile = lds_addr(buf) + off;
   const int lane = threadIdx.x & 63;
   const int cvar = (lane & 15) >> 2;              // chunk of dim 16t + l%16 is 4t + cvar
 #pragma unroll
@@ -360,22 +363,23 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
   cur.T = misc[10] + cur.kvh * cur.n;
 
   // ---- tile stream: the wave's k-th tile is global tile t_begin + wave + kWaves k,
-  // copied into buffer k & 1; copies run two tiles ahead, across segments --------
+  // copied into buffer k & 1; the copy of tile k + 1 starts as tile k is
+  // computed, across segments ------------------------------------------------------
   const uint32_t smem0 = lds_addr(smem);
   const uint32_t tiles = smem0 + wave * C::kBufs * C::kTileBytes;
+  lds_char* const tile_buf = (lds_char*)smem + wave * C::kBufs * C::kTileBytes;
   const uint32_t span = static_cast<uint32_t>(a.cache_cap) * C::kRowBytes;   // < 2^31 (checked on the host)
   Seg pf = cur;
-  auto issue = [&](int k) {
+  auto issue = [&](lds_char* dst, int k) {
     const int g = t_begin + wave + C::kWaves * k;
     if (g >= t_end) return;
     while (g >= pf.T + pf.n) seg_next(pf, a);
     const int64_t head = static_cast<int64_t>(pf.b) * a.n_kv_heads + pf.kvh;
     const BufRsrc rk = make_rsrc(static_cast<const char*>(a.k_cache) + head * span, span);
     const BufRsrc rv = SHARED ? rk : make_rsrc(static_cast<const char*>(a.v_cache) + head * span, span);
-    issue_tile<C>(tiles + (k & 1) * C::kTileBytes, rk, rv, (g - pf.T) * C::KT, pf.keys, lane);
+    issue_tile<C>(dst, rk, rv, (g - pf.T) * C::KT, pf.keys, lane);
   };
-  issue(0);
-  issue(1);
+  issue(tile_buf, 0);
 
   // ---- rotation rates of the lane's pairs lane + 64 m (fp64, one exp2 each) ------
   constexpr int kPairsPerLane = D / 128;
@@ -410,7 +414,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
 
   const int hcol = lane & 15, kg = lane >> 4;
   const uint32_t k_lane = key_lane_base<C, T>(tiles, lane);
-  const uint32_t v_lane = value_lane_base<C, T>(tiles + (SHARED ? 0 : C::kKBytes), lane);
+  const uint32_t v_off = value_lane_base<C, T>(SHARED ? 0 : C::kKBytes, lane);   // within a buffer
   const uint32_t q_lane = smem0 + C::kQOff + lane * 8 * C::kSz;
   const uint32_t fine_lane = smem0 + C::kFineOff + (hcol * C::kRot + 4 * kg) * 8;
   const uint32_t coarse_lane = coarse_s + 4 * kg * 8;
@@ -492,74 +496,78 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
       if (g >= p_end) break;
       const int key0 = (g - cur.T) * C::KT;
       const uint32_t buf = (k & 1) * C::kTileBytes;
-      // tile k has landed once at most the next tile's copies are in flight
-      if (g + C::kWaves < t_end) wait_vm_le<C::kDmaPerTile>();
-      else wait_vm_le<0>();
+      wait_vm_le<0>();   // tile k has landed: it is the wave's only copy in flight
+      // The step runs in a function whose two buffers are restrict pointers:
+      // the compiler then knows the copy of tile k + 1 into `nxt` does not
+      // feed the reads of `cur_buf`, and adds no wait for it before them.
+      auto step = [&](const lds_char* __restrict__ cur_buf, lds_char* __restrict__ nxt) {
+        issue(nxt, k + 1);
 
-      // S^T = K~ Q~^T; the lane's A operand is key row hcol, dims 32u + 8kg .. +7.
-      // Reads run kQAhead steps ahead of the MFMAs.
-      QkStep<T> st[kQAhead + 1];
-#pragma unroll
-      for (int u = 0; u < kQAhead; ++u) load_step<C>(st[u], u, k_lane + buf, q_lane, coarse_lane, fine_lane);
-      f32x4 sa = f32x4{}, sb = f32x4{};
-#pragma unroll
-      for (int u = 0; u < C::kQSteps; ++u) {
-        if (u + kQAhead < C::kQSteps)
-          load_step<C>(st[(u + kQAhead) % (kQAhead + 1)], u + kQAhead, k_lane + buf, q_lane, coarse_lane, fine_lane);
-        QkStep<T>& cs = st[u % (kQAhead + 1)];
-        if (u < C::kRotSteps) rotate_step(cs);
-        mma16((u & 1) ? sb : sa, cs.kf, cs.qf);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      f32x4 s = sa + sb;
-      if constexpr (SHARED) {   // publish the wave's next tile's coarse angles
-        const f32x2 c = coarse_l;
-        coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
-        coarse_l[1] = c[1] * step_l[0] + c[0] * step_l[1];
-        lds_st<f32x2>(coarse_s + lane * 8, coarse_l);   // read next tile, after the fence below
-      }
+        // S^T = K~ Q~^T; the lane's A operand is key row hcol, dims 32u + 8kg .. +7.
+        // Reads run kQAhead steps ahead of the MFMAs.
+        QkStep<T> st[kQAhead + 1];
+  #pragma unroll
+        for (int u = 0; u < kQAhead; ++u) load_step<C>(st[u], u, k_lane + buf, q_lane, coarse_lane, fine_lane);
+        f32x4 sa = f32x4{}, sb = f32x4{};
+  #pragma unroll
+        for (int u = 0; u < C::kQSteps; ++u) {
+          if (u + kQAhead < C::kQSteps)
+            load_step<C>(st[(u + kQAhead) % (kQAhead + 1)], u + kQAhead, k_lane + buf, q_lane, coarse_lane, fine_lane);
+          QkStep<T>& cs = st[u % (kQAhead + 1)];
+          if (u < C::kRotSteps) rotate_step(cs);
+          mma16((u & 1) ? sb : sa, cs.kf, cs.qf);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        f32x4 s = sa + sb;
+        if constexpr (SHARED) {   // publish the wave's next tile's coarse angles
+          const f32x2 c = coarse_l;
+          coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
+          coarse_l[1] = c[1] * step_l[0] + c[0] * step_l[1];
+          lds_st<f32x2>(coarse_s + lane * 8, coarse_l);   // read next tile, after the fence below
+        }
 
-      // online softmax; lane holds keys 4*kg + v of head column hcol
-      float mt = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        if (key0 + 4 * kg + v >= cur.keys) s[v] = -INFINITY;
-        mt = fmaxf(mt, s[v]);
-      }
-      mt = max_across_kg(mt);
-      const bool rescale = __any(mt > m_run + kTau);
-      const float m_new = rescale ? fmaxf(m_run, mt) : m_run;
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      m_run = m_new;
-      Frag4<T> pf4;
-      float psum = 0.f;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = __builtin_amdgcn_exp2f(s[v] - m_use);
-        psum += p;
-        frag_set(pf4, v, p);
-      }
-      if (rescale) {
-#pragma unroll
-        for (int t = 0; t < C::kDBlocks; ++t) o[t] *= alpha;
-        l_part *= alpha;
-      }
-      l_part += psum;
+        // online softmax; lane holds keys 4*kg + v of head column hcol
+        float mt = -INFINITY;
+  #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (key0 + 4 * kg + v >= cur.keys) s[v] = -INFINITY;
+          mt = fmaxf(mt, s[v]);
+        }
+        mt = max_across_kg(mt);
+        const bool rescale = __any(mt > m_run + kTau);
+        const float m_new = rescale ? fmaxf(m_run, mt) : m_run;
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        m_run = m_new;
+        Frag4<T> pf4;
+        float psum = 0.f;
+  #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p = __builtin_amdgcn_exp2f(s[v] - m_use);
+          psum += p;
+          frag_set(pf4, v, p);
+        }
+        if (rescale) {
+  #pragma unroll
+          for (int t = 0; t < C::kDBlocks; ++t) o[t] *= alpha;
+          l_part *= alpha;
+        }
+        l_part += psum;
 
-      // O^T += V^T P^T, reads kVAhead blocks ahead
-      Frag4<T> vf[kVAhead];
-#pragma unroll
-      for (int t = 0; t < kVAhead; ++t) value_frag<C>(vf[t], v_lane + buf, t);
-#pragma unroll
-      for (int t = 0; t < C::kDBlocks; ++t) {
-        const Frag4<T> vc = vf[t % kVAhead];
-        if (t + kVAhead < C::kDBlocks) value_frag<C>(vf[t % kVAhead], v_lane + buf, t + kVAhead);
-        mma16k16(o[t], vc, pf4);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      lds_fence();   // this tile's LDS reads are done before its buffer is refilled
-      issue(k + 2);
+        // O^T += V^T P^T, reads kVAhead blocks ahead
+        Frag4<T> vf[kVAhead];
+  #pragma unroll
+        for (int t = 0; t < kVAhead; ++t) value_frag<C>(vf[t], cur_buf, v_off, t);
+  #pragma unroll
+        for (int t = 0; t < C::kDBlocks; ++t) {
+          const Frag4<T> vc = vf[t % kVAhead];
+          if (t + kVAhead < C::kDBlocks) value_frag<C>(vf[t % kVAhead], cur_buf, v_off, t + kVAhead);
+          mma16k16(o[t], vc, pf4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_fence();   // this tile's LDS reads are done before its buffer is refilled
+      };
+      step(tile_buf + buf, tile_buf + (buf ^ C::kTileBytes));
     }
 
     // ---- this wave's partial result for the segment --------------------------------
