@@ -77,6 +77,9 @@ typedef __amdgpu_buffer_rsrc_t BufRsrc;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)p));
 }
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
 template <typename V>
 __device__ __forceinline__ V lds_ld(uint32_t addr) {
   return *(const __attribute__((address_space(3))) V*)(static_cast<uintptr_t>(addr));
