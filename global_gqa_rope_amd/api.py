@@ -147,6 +147,32 @@ def gemma_attn_decode(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens, max_s
     return out
 
 
+def gemma_attn_decode_multi_workspace_size(layer: Layer, batch: int, q_len: int, max_seq_len: int) -> int:
+    return int(_lib.load().gemma_attn_decode_multi_workspace_size(ctypes.byref(layer.struct()), batch, q_len,
+                                                                    max_seq_len))
+
+
+def gemma_attn_decode_multi(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens, max_seq_len: int,
+                            out=None, ws=None, stream=None) -> torch.Tensor:
+    """q [B, q_len, Hq, d]: the last q_len positions of each sequence against its cache."""
+    B, T, Hq, d = q.shape
+    Hkv = layer.n_kv_heads
+    cap = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(gemma_attn_decode_multi_workspace_size(layer, B, T, max_seq_len), q.device)
+    st = _lib.load().gemma_attn_decode_multi(
+        ctypes.byref(layer.struct()), B, T, _ptr(q, "q", layer, (B, T, Hq, d)),
+        _ptr(q_gain, "q_gain", layer, (d,)), _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d)),
+        _ptr(v_cache, "v_cache", layer, (B, Hkv, cap, d)), cap,
+        _ptr(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,)), int(max_seq_len),
+        _ptr(out, "out", layer, (B, T, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8), ws.numel(),
+        _stream(stream))
+    _lib.check(st)
+    return out
+
+
 # ---- kernel timing hooks ------------------------------------------------------
 KERNEL_IDS = {"prefill_attn": 0, "prefill_prep": 1, "decode_splitk": 2, "decode_merge": 3,
               "kv_append": 4}

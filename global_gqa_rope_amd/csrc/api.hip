@@ -166,15 +166,29 @@ int decode_tiles_per_seq(const ga_layer* L, int max_seq_len) {
 // depend on the device; the launch then uses one workgroup per CU at most.
 constexpr int kMaxDecodeCUs = 1 << 20;
 
-bool decode_plan(const ga_layer* L, const Derived& dv, int batch, int max_seq_len, int n_cus, ga::DecodePlan* plan) {
+bool decode_plan(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len, int n_cus,
+                 ga::DecodePlan* plan) {
   return ga::plan_decode(L->dtype, L->head_dim, dv.group, L->kv_shared, batch, L->n_kv_heads,
-                         decode_tiles_per_seq(L, max_seq_len), n_cus, plan);
+                         decode_tiles_per_seq(L, max_seq_len), n_cus, q_len, plan);
 }
 
-size_t decode_bytes(const ga_layer* L, const Derived& dv, int batch, int max_seq_len) {
+size_t decode_bytes(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len) {
   ga::DecodePlan plan;
-  if (!decode_plan(L, dv, batch, max_seq_len, kMaxDecodeCUs, &plan)) return 0;
+  if (!decode_plan(L, dv, batch, q_len, max_seq_len, kMaxDecodeCUs, &plan)) return 0;
   return align_up(plan.bytes());
+}
+
+// The query tokens of one decode call fill the 16 columns of the QK^T MFMA:
+// q_len tokens x G heads must fit.  Several tokens at once are built for the
+// global K=V layers; a windowed layer's ring of W slots no longer holds keys
+// that an earlier one of several new tokens would see.
+ga_status check_q_len(const ga_layer* L, const Derived& dv, int q_len) {
+  if (q_len < 1) return fail(GA_EINVAL, "q_len must be >= 1");
+  if (q_len * dv.group > 16)
+    return fail(GA_EUNSUPPORTED, "q_len %d x %d query heads per KV head exceeds 16 query columns", q_len, dv.group);
+  if (q_len > 1 && (L->window > 0 || !L->kv_shared))
+    return fail(GA_EUNSUPPORTED, "q_len > 1 is built for global K=V layers only");
+  return GA_OK;
 }
 
 ga_status check_workspace(void* ws, size_t have, size_t need) {
@@ -245,9 +259,15 @@ size_t gemma_attn_prefill_workspace_size(const ga_layer* layer, int32_t batch, i
 }
 
 size_t gemma_attn_decode_workspace_size(const ga_layer* layer, int32_t batch, int32_t max_seq_len) {
+  return gemma_attn_decode_multi_workspace_size(layer, batch, 1, max_seq_len);
+}
+
+size_t gemma_attn_decode_multi_workspace_size(const ga_layer* layer, int32_t batch, int32_t q_len,
+                                              int32_t max_seq_len) {
   Derived dv;
   if (check_layer(layer, &dv) != GA_OK || batch < 0 || max_seq_len < 1) return 0;
-  return decode_bytes(layer, dv, batch, max_seq_len);
+  if (check_q_len(layer, dv, q_len) != GA_OK) return 0;
+  return decode_bytes(layer, dv, batch, q_len, max_seq_len);
 }
 
 ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_len, const void* q,
@@ -330,10 +350,20 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
                             const void* k_cache, const void* v_cache, int32_t cache_cap,
                             const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
                             size_t workspace_bytes, void* stream) {
+  return gemma_attn_decode_multi(layer, batch, 1, q, q_gain, k_cache, v_cache, cache_cap, seq_lens, max_seq_len,
+                                 out, workspace, workspace_bytes, stream);
+}
+
+ga_status gemma_attn_decode_multi(const ga_layer* layer, int32_t batch, int32_t q_len, const void* q,
+                                  const void* q_gain, const void* k_cache, const void* v_cache, int32_t cache_cap,
+                                  const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   Derived dv;
   ga_status st = check_layer(layer, &dv);
   if (st != GA_OK) return st;
   if (batch < 0) return fail(GA_EINVAL, "batch must be >= 0");
+  st = check_q_len(layer, dv, q_len);
+  if (st != GA_OK) return st;
   if (batch == 0) return GA_OK;
   if (max_seq_len < 1) return fail(GA_EINVAL, "max_seq_len must be >= 1");
   if (static_cast<int64_t>(batch) * layer->n_kv_heads * decode_tiles_per_seq(layer, max_seq_len) > INT32_MAX)
@@ -346,7 +376,7 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
   if (st != GA_OK) return st;
   if (static_cast<int64_t>(cache_cap) * layer->head_dim * dv.elem > INT32_MAX)
     return fail(GA_EUNSUPPORTED, "cache_cap %d: one head's cache must stay under 2 GiB for decode", cache_cap);
-  const size_t need = decode_bytes(layer, dv, batch, max_seq_len);
+  const size_t need = decode_bytes(layer, dv, batch, q_len, max_seq_len);
   st = check_workspace(workspace, workspace_bytes, need);
   if (st != GA_OK) return st;
   int dev = 0, cus = 0;
@@ -354,7 +384,7 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
   if (he == hipSuccess) he = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (he != hipSuccess) return hip_status(he, "decode: device query");
   ga::DecodePlan plan;
-  if (!decode_plan(layer, dv, batch, max_seq_len, cus, &plan))
+  if (!decode_plan(layer, dv, batch, q_len, max_seq_len, cus, &plan))
     return fail(GA_EUNSUPPORTED, "no decode kernel for this layer configuration");
   ga::DecodeArgs da{};
   da.q = q; da.q_gain = q_gain; da.k_cache = k_cache; da.v_cache = v_cache; da.seq_lens = seq_lens;
@@ -363,6 +393,7 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch, const void* q,
   da.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.prefix_bytes);
   da.batch = batch; da.n_q_heads = layer->n_q_heads; da.n_kv_heads = layer->n_kv_heads; da.n_rot = dv.n_rot;
   da.window = layer->window; da.cache_cap = cache_cap; da.max_seq_len = max_seq_len; da.n_wgs = plan.n_wgs;
+  da.q_len = q_len; da.slot_floats = static_cast<int>(plan.slot_floats);
   da.eps = layer->norm_eps; da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
   return hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
                                       static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),

@@ -103,7 +103,7 @@ __device__ __forceinline__ void wait_vm_le() { asm volatile("s_waitcnt vmcnt(%0)
 // Sequence b's number of readable keys, or -1 if its length is out of range.
 __device__ __forceinline__ int decode_keys(const DecodeArgs& a, int b) {
   const int L = a.seq_lens[b];
-  if (L < 1 || L > a.max_seq_len) return -1;
+  if (L < a.q_len || L < 1 || L > a.max_seq_len) return -1;
   if (a.window == 0 && L > a.cache_cap) return -1;
   return a.window > 0 ? min(L, a.window) : L;
 }
@@ -309,7 +309,8 @@ template <typename T, int D, int G, bool SHARED>
 __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, G, SHARED>;
   static_assert(C::KT == kDecodeTile, "tile size");
-  constexpr int kSlot = G * D + 64;
+  const int kSlot = a.slot_floats;
+  const int ncol = G * a.q_len;   // query columns: column c is token c / G, head c % G (<= 16)
   __shared__ __attribute__((aligned(4096))) char smem[C::kLdsBytes];
 
   const int wg = blockIdx.x, P = gridDim.x;
@@ -432,27 +433,32 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
     const int p_end = min(cur.T + cur.n, t_end);
     __syncthreads();   // the previous segment's reads of the query operand are done
 
-    // ---- query prep: QKNorm + rotation at qpos, written in operand order ------
-    // Operand fragment u, lane hcol + 16 kg, element j = q~[hcol][32u + 8kg + j]
-    // (heads >= G are zeros).  One wave per head: lane owns pairs lane + 64 m.
+    // ---- query prep: QKNorm + rotation at each token's position, written in
+    // operand order.  Operand fragment u, lane hcol + 16 kg, element j =
+    // q~[hcol][32u + 8kg + j]; column c is token c / G (position
+    // L - q_len + c / G) and head c % G of the group; columns >= G q_len are
+    // zeros.  One wave per column: lane owns pairs lane + 64 m.
     {
-      const int qpos = a.seq_lens[cur.b] - 1;
-      const T* __restrict__ q =
-          static_cast<const T*>(a.q) + (static_cast<int64_t>(cur.b) * a.n_q_heads + cur.kvh * G) * D;
-      f32x2 qcs[kPairsPerLane];
-#pragma unroll
-      for (int m = 0; m < kPairsPerLane; ++m)
-        qcs[m] = (lane + 64 * m < a.n_rot) ? rope_cos_sin(static_cast<double>(qpos) * w_pair[m]) : f32x2{1.f, 0.f};
+      const int L = a.seq_lens[cur.b];
       for (int h = wave; h < 16; h += C::kWaves) {
+        const int tok = h / G;
+        const T* __restrict__ q = static_cast<const T*>(a.q) +
+            ((static_cast<int64_t>(cur.b) * a.q_len + (h < ncol ? tok : 0)) * a.n_q_heads + cur.kvh * G + h % G) * D;
         float x[kPairsPerLane][2];
+        f32x2 qcs[kPairsPerLane];
         float rstd = 0.f;
-        if (h < G) {
+        if (h < ncol) {
+          const int qpos = L - a.q_len + tok;
+#pragma unroll
+          for (int m = 0; m < kPairsPerLane; ++m)
+            qcs[m] = (lane + 64 * m < a.n_rot) ? rope_cos_sin(static_cast<double>(qpos) * w_pair[m])
+                                               : f32x2{1.f, 0.f};
           float ss = 0.f;
 #pragma unroll
           for (int m = 0; m < kPairsPerLane; ++m) {
             const int pr = lane + 64 * m;
-            x[m][0] = to_f32(q[h * D + 2 * pr]);
-            x[m][1] = to_f32(q[h * D + 2 * pr + 1]);
+            x[m][0] = to_f32(q[2 * pr]);
+            x[m][1] = to_f32(q[2 * pr + 1]);
             ss += x[m][0] * x[m][0] + x[m][1] * x[m][1];
           }
 #pragma unroll
@@ -463,7 +469,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
         for (int m = 0; m < kPairsPerLane; ++m) {
           const int pr = lane + 64 * m;
           float x0 = 0.f, x1 = 0.f;
-          if (h < G) {
+          if (h < ncol) {
             x0 = x[m][0] * rstd * to_f32(gq[2 * pr]);
             x1 = x[m][1] * rstd * to_f32(gq[2 * pr + 1]);
             rotate_pair(x0, x1, qcs[m]);
@@ -493,6 +499,8 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
 #pragma unroll
     for (int t = 0; t < C::kDBlocks; ++t) o[t] = f32x4{};
     float m_run = -INFINITY, l_part = 0.f;
+    // keys the lane's column sees: token j of q_len sits at position L - q_len + j
+    const int key_lim = cur.keys - ((hcol < ncol) ? a.q_len - 1 - hcol / G : 0);
 
     for (;; ++k) {
       const int g = t_begin + wave + C::kWaves * k;
@@ -533,7 +541,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
         float mt = -INFINITY;
   #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          if (key0 + 4 * kg + v >= cur.keys) s[v] = -INFINITY;
+          if (key0 + 4 * kg + v >= key_lim) s[v] = -INFINITY;
           mt = fmaxf(mt, s[v]);
         }
         mt = max_across_kg(mt);
@@ -579,10 +587,10 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
     // previous workgroup's end.  A wave without tiles here leaves m = -inf.
     const float l = sum_across_kg(l_part);
     float* slot = a.partials + static_cast<size_t>(C::kWaves * (wg + seg) + wave) * kSlot;
-    if (hcol < G) {
+    if (hcol < ncol) {
 #pragma unroll
       for (int t = 0; t < C::kDBlocks; ++t) *reinterpret_cast<f32x4*>(slot + hcol * D + 16 * t + 4 * kg) = o[t];
-      if (kg == 0) *reinterpret_cast<f32x2*>(slot + G * D + 2 * hcol) = f32x2{m_run, l};
+      if (kg == 0) *reinterpret_cast<f32x2*>(slot + ncol * D + 2 * hcol) = f32x2{m_run, l};
     }
     wait_vm_le<0>();   // stores retired: later tile waits count copies only
     if (p_end >= t_end) break;
@@ -590,20 +598,22 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
   }
 }
 
-// Log-sum-exp merge of one (sequence, query head): the partials of the waves of
+// Log-sum-exp merge of one (sequence, query column): the partials of the waves of
 // every workgroup that streamed the segment.  Their weights exp2(m_i - M) go to
 // LDS once; then each thread accumulates whole head dims (consecutive threads,
 // consecutive dims).  Invalid lengths get a NaN row.
 template <typename T, int D, int G, bool SHARED>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, G, SHARED>;
-  constexpr int kSlot = G * D + 64;
+  const int kSlot = a.slot_floats;
+  const int ncol = G * a.q_len;
   __shared__ float wgt[1024];
   __shared__ float red[256];
-  const int seg = blockIdx.x / G, h = blockIdx.x % G;
+  const int seg = blockIdx.x / ncol, h = blockIdx.x % ncol;   // h: column (token h / G, head h % G)
   const int b = seg / a.n_kv_heads, kvh = seg % a.n_kv_heads;
   const int t = threadIdx.x;
-  T* __restrict__ out = static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.n_q_heads + kvh * G + h) * D;
+  T* __restrict__ out = static_cast<T*>(a.out) +
+      ((static_cast<int64_t>(b) * a.q_len + h / G) * a.n_q_heads + kvh * G + h % G) * D;
   const int keys = decode_keys(a, b);
   if (keys < 0) {
     for (int d = t; d < D; d += 256) out[d] = from_f32<T>(NAN);
@@ -627,7 +637,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
   float mx = -INFINITY;
   for (int i = t; i < count; i += 256)
-    if (written(i)) mx = fmaxf(mx, slot(i)[G * D + 2 * h]);
+    if (written(i)) mx = fmaxf(mx, slot(i)[ncol * D + 2 * h]);
   red[t] = mx;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -641,9 +651,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     float w = 0.f;
     if (written(i)) {
       const float* p = slot(i);
-      const float mi = p[G * D + 2 * h];
+      const float mi = p[ncol * D + 2 * h];
       w = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - M);
-      lsum += w * p[G * D + 2 * h + 1];
+      lsum += w * p[ncol * D + 2 * h + 1];
     }
     wgt[i] = w;
   }
@@ -671,8 +681,8 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t s, LaunchTimer tim
   if (timer) timer(s, 2, false);
   if (e != hipSuccess) return e;
   if (timer) timer(s, 3, true);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, G, SHARED>), dim3(a.batch * a.n_kv_heads * G), dim3(256), 0, s,
-                     a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, G, SHARED>), dim3(a.batch * a.n_kv_heads * G * a.q_len), dim3(256),
+                     0, s, a);
   e = hipGetLastError();
   if (timer) timer(s, 3, false);
   return e;
@@ -709,7 +719,7 @@ static int waves_of() {
 }
 
 bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, int n_kv_heads,
-                 int max_tiles_per_seq, int n_cus, DecodePlan* plan) {
+                 int max_tiles_per_seq, int n_cus, int q_len, DecodePlan* plan) {
   int waves = 0;
   if (dtype == 0 && head_dim == 512) waves = kv_shared ? waves_of<bf16, 512, true>() : waves_of<bf16, 512, false>();
   if (dtype == 0 && head_dim == 256) waves = kv_shared ? waves_of<bf16, 256, true>() : waves_of<bf16, 256, false>();
@@ -728,7 +738,7 @@ bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, i
   plan->n_wgs = static_cast<int>(wgs < 1 ? 1 : wgs);
   plan->prefix_bytes = (static_cast<size_t>(batch + 1) * 4 + 255) / 256 * 256;
   plan->slots = static_cast<size_t>(waves) * (plan->n_wgs + static_cast<size_t>(batch) * n_kv_heads);
-  plan->slot_floats = static_cast<size_t>(group) * head_dim + 64;
+  plan->slot_floats = static_cast<size_t>(q_len) * group * head_dim + 64;
   return true;
 }
 

@@ -67,8 +67,10 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   void* out;
   int32_t* tile_prefix;    // [B + 1] tiles of the sequences before b (written by the split-K kernel)
-  float* partials;         // [slots][G * D + 64] fp32: o, then (m, l) per head
+  float* partials;         // [slots][slot_floats] fp32: o per column, then (m, l) per column
   int batch, n_q_heads, n_kv_heads, n_rot, window, cache_cap, max_seq_len;
+  int q_len;               // query tokens per sequence: the last q_len positions (1 = one token)
+  int slot_floats;         // q_len * G * D + 64
   int n_wgs;               // split-K workgroups (the grid)
   float eps;
   float qk_scale_log2;
@@ -85,7 +87,7 @@ struct DecodePlan {
 };
 // Returns false if the configuration has no decode kernel.
 bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, int n_kv_heads,
-                 int max_tiles_per_seq, int n_cus, DecodePlan* plan);
+                 int max_tiles_per_seq, int n_cus, int q_len, DecodePlan* plan);
 
 hipError_t launch_rope_table(void* table, int n_pos, int n_rot, int head_dim, double log2_theta,
                              hipStream_t s);

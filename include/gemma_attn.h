@@ -171,6 +171,36 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * Multi-token decode: the last q_len positions of each sequence attend to its
+ * cache in one pass, each causally (token j at position seq_lens[b] - q_len + j
+ * sees keys 0 .. its own position).  This is the step in which the main model
+ * checks the tokens its multi-token-prediction drafter proposed ("Gemma 4
+ * Technical Report (translated notes)", section 2.6, MTP drafter); the cache
+ * is streamed once for all q_len tokens.  The new tokens' keys must already be
+ * in the cache (kv_append for each, or a prefill).
+ *
+ *   q        [B, q_len, Hq, d] raw queries of the new tokens
+ *   out      [B, q_len, Hq, d]
+ *   seq_lens device int32 [B]: valid keys including the q_len new tokens; a
+ *            sequence with L_b < q_len gets NaN rows like an invalid length.
+ *   other arguments as for gemma_attn_decode, with the workspace from
+ *   gemma_attn_decode_multi_workspace_size().
+ * q_len = 1 is gemma_attn_decode.  GA_EINVAL for q_len < 1; GA_EUNSUPPORTED
+ * when q_len * (Hq / Hkv) > 16 (the query columns of one pass) or when
+ * q_len > 1 on a layer other than a global K=V one (a windowed layer's ring
+ * of W slots has already dropped keys that the earlier of the new tokens
+ * would see).
+ */
+size_t gemma_attn_decode_multi_workspace_size(const ga_layer* layer, int32_t batch,
+                                              int32_t q_len, int32_t max_seq_len);
+ga_status gemma_attn_decode_multi(const ga_layer* layer, int32_t batch, int32_t q_len,
+                                  const void* q, const void* q_gain,
+                                  const void* k_cache, const void* v_cache,
+                                  int32_t cache_cap, const int32_t* seq_lens,
+                                  int32_t max_seq_len, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Measurement hooks (not part of the computation).  While enabled, every
  * launch of the kernels below is bracketed by a pair of HIP events recorded
  * on the caller's stream; gemma_attn_profile_read() waits for the recorded

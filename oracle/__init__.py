@@ -33,6 +33,7 @@ from .attention import (  # noqa: F401
     OracleLayer,
     cache_bytes_per_token,
     decode_from_cache,
+    decode_multi_from_cache,
     expected_caches_after_append,
     expected_caches_after_prefill,
     masked_softmax_attention,

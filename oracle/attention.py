@@ -283,6 +283,42 @@ def decode_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
     return np.stack(out)
 
 
+def decode_multi_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
+                            batches=None) -> np.ndarray:
+    """Several new tokens per sequence against the cache, each causally.
+
+    q [B,T,Hq,d] raw; token j of sequence b sits at position L_b - T + j, where
+    ``seq_lens[b]`` = L_b counts the valid keys including all T new tokens, and
+    attends to cache slots 0 .. its own position (global layers only: slot =
+    position; the K=V cache's unrotated keys are rotated on the fly and used
+    unrotated as values).  This is the check of tokens proposed by the MTP
+    drafter ("Gemma 4 Technical Report" notes, section 2.6): each is attention
+    at its own position, the definition of ``prefill`` row by row.  Returns
+    out [len(batches), T, Hq, d].
+    """
+    if layer.window or not layer.kv_shared:
+        raise ValueError("several new tokens at once are defined here for global K=V layers only")
+    G, T = layer.group, q.shape[1]
+    batches = range(q.shape[0]) if batches is None else batches
+    out = []
+    for b in batches:
+        L = int(seq_lens[b])
+        if L < T:
+            raise ValueError("fewer keys than new tokens")
+        qpos = L - T + np.arange(T)
+        q_hat = qk_norm(q[b], g_q, layer.norm_eps)                             # [T,Hq,d]
+        q_rot = rotate(q_hat, qpos[:, None], layer.rope_theta, layer.rope_fraction)
+        kpos = np.arange(L)
+        rows = np.empty((T, layer.n_q_heads, layer.head_dim))
+        for c in range(layer.n_kv_heads):
+            keys = _f64(k_cache[b, c, :L])
+            k_rot = rotate(keys, kpos, layer.rope_theta, layer.rope_fraction)
+            for h in range(c * G, (c + 1) * G):
+                rows[:, h] = masked_softmax_attention(q_rot[:, h], qpos, k_rot, keys, kpos, layer.scale, 0)
+        out.append(rows)
+    return np.stack(out)
+
+
 def cache_bytes_per_token(head_dim: int, fraction: float, layout: str,
                           bytes_per_elem: float = 1.0) -> float:
     """Bytes one KV head caches per token under three global-layer layouts.

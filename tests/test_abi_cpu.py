@@ -112,6 +112,25 @@ def test_decode_and_append_validation(lib):
     assert app(layer=loc, v=FAKE, vc=None, cap=1024) == 1
 
 
+def test_multi_token_decode_validation(lib):
+    g = L()                                                     # global K=V, G = 8
+    loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
+    dec = lambda **kw: lib.gemma_attn_decode_multi(
+        ctypes.byref(kw.get("layer", g)), 2, kw.get("T", 2), FAKE, FAKE, FAKE, kw.get("v", None),
+        kw.get("cap", 4096), FAKE, 4096, FAKE, FAKE, 1 << 40, None)
+    assert dec(T=0) == 1                                        # q_len >= 1
+    assert dec(T=3) == 2                                        # 3 tokens x 8 heads > 16 columns
+    assert "16 query columns" in lib.gemma_attn_last_error().decode()
+    assert dec(layer=loc, T=2, v=FAKE, cap=1024) == 2           # windowed layers take one token
+    wsz = lambda layer, B, T, n: lib.gemma_attn_decode_multi_workspace_size(ctypes.byref(layer), B, T, n)
+    assert wsz(g, 2, 0, 4096) == 0 and wsz(g, 2, 3, 4096) == 0 and wsz(loc, 2, 2, 4096) == 0
+    # one token is the single-token call; two tokens widen every slot to 2 G d outputs
+    assert wsz(g, 2, 1, 4096) == lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 4096)
+    assert wsz(g, 2, 2, 4096) == decode_ws(2, 4, 16, 512, 4096)
+    g2 = L(hq=8, hkv=4, d=512, shared=1)                         # G = 2: up to 8 tokens
+    assert wsz(g2, 3, 8, 1000) == decode_ws(3, 4, 16, 512, 1000)
+
+
 def test_workspace_sizes_follow_the_layout(lib):
     g = L()
     # table (S_pad * 64 pairs * 8 B) + key rows [B,Hkv,S_pad,128] (the rotated

@@ -179,6 +179,55 @@ def test_decode_invalid_lengths_write_nan_rows():
     assert_close(out[1:2], ref, torch.bfloat16, "valid row next to invalid ones")
 
 
+# ---- several new tokens per sequence at once (global K=V layers) ---------------------
+
+def _multi_case(shape, lens, T, seed, dtype=torch.bfloat16):
+    dev = device()
+    B, D, cap = len(lens), shape.head_dim, max(lens)
+    kc = W.normal((B, shape.n_kv_heads, cap, D), seed, "k_cache", dtype, "cpu")
+    q = W.normal((B, T, shape.n_q_heads, D), seed, "q_dec", dtype, "cpu")
+    g_q = W.gains(D, seed, "g_q", False, dtype)
+    seq = torch.tensor(lens, dtype=torch.int32)
+    out = torch.full((B, T, shape.n_q_heads, D), float("nan"), dtype=dtype, device=dev)
+    api.gemma_attn_decode_multi(api_layer(shape, dtype), q.to(dev), g_q.to(dev), kc.to(dev), None, seq.to(dev),
+                                max(lens), out=out)
+    torch.cuda.synchronize()
+    return q, g_q, kc, seq, out
+
+
+@pytest.mark.parametrize("hq,T,lens", [
+    (32, 2, [2, 17, 1024, 1025, 2600]),     # G = 8: 16 columns
+    (16, 3, [3, 40, 1500]),                  # G = 4: 12 columns, 4 padding
+    (8, 8, [8, 33, 700, 2049]),              # G = 2: 16 columns
+    (32, 1, [1, 100, 3000]),                 # one token through the multi-token call
+])
+def test_multi_token_decode_bf16(hq, T, lens):
+    shape = W.replace(W.GLOBAL_LAYER, n_q_heads=hq)
+    q, g_q, kc, seq, out = _multi_case(shape, lens, T, seed=13)
+    ref = O.decode_multi_from_cache(oracle_layer(shape), to64(q), to64(g_q), to64(kc), None, seq.numpy())
+    assert_close(out, ref, torch.bfloat16, f"multi-token decode G={hq // 4} T={T} {lens}")
+
+
+def test_multi_token_decode_of_one_token_equals_decode():
+    shape = W.GLOBAL_LAYER
+    lens = [1, 555, 4100]
+    q, g_q, kc, seq, out = _multi_case(shape, lens, 1, seed=21)
+    dev = device()
+    one = api.gemma_attn_decode(api_layer(shape, torch.bfloat16), q[:, 0].to(dev), g_q.to(dev), kc.to(dev), None,
+                                seq.to(dev), max(lens))
+    assert torch.equal(out[:, 0].cpu(), one.cpu()), "q_len = 1 must take exactly the single-token path"
+
+
+def test_multi_token_decode_short_sequences_write_nan_rows():
+    shape = W.GLOBAL_LAYER
+    q, g_q, kc, seq, out = _multi_case(shape, [1, 2, 300], 2, seed=5)     # L = 1 < q_len = 2
+    o = out.float().cpu()
+    assert torch.isnan(o[0]).all()
+    ref = O.decode_multi_from_cache(oracle_layer(shape), to64(q), to64(g_q), to64(kc), None, seq.numpy(),
+                                    batches=[1, 2])
+    assert_close(out[1:], ref, torch.bfloat16, "valid sequences next to a short one")
+
+
 def test_kv_append_ignores_out_of_range_positions():
     shape = W.GLOBAL_LAYER
     dev = device()
@@ -294,6 +343,28 @@ def test_global_decode_full_size_sampled():
     wl = W.CONFIGS["global_decode"]
     lens = wl.lengths().numpy()
     _sampled_decode(wl, [int(np.argmin(lens)), int(np.argmax(lens))], "global decode B16")
+
+
+def test_multi_token_decode_full_size_sampled():
+    """Two new tokens per sequence on the global decode workload (B=16,
+    contexts up to 128K): the shortest and the longest sequence against the oracle."""
+    wl = W.CONFIGS["global_decode"]
+    shape, dev = wl.layer, device()
+    lens = wl.lengths()
+    B, cap, D, T = wl.batch, wl.cache_cap(), shape.head_dim, 2
+    kc = W.normal((B, shape.n_kv_heads, cap, D), wl.seed, "k_cache", torch.bfloat16, dev)
+    q = W.normal((B, T, shape.n_q_heads, D), wl.seed, "q_dec", torch.bfloat16, dev)
+    g_q = W.gains(D, wl.seed, "g_q", False, torch.bfloat16, dev)
+    out = api.gemma_attn_decode_multi(api_layer(shape, torch.bfloat16), q, g_q, kc, None, lens.to(dev),
+                                      int(lens.max()))
+    torch.cuda.synchronize()
+    ol = oracle_layer(shape)
+    for b in [int(np.argmin(lens.numpy())), int(np.argmax(lens.numpy()))]:
+        L = int(lens[b])
+        ref = O.decode_multi_from_cache(ol, to64(q[b:b + 1]), to64(g_q), to64(kc[b:b + 1, :, :L]), None,
+                                        np.array([L]))
+        assert_close(out[b:b + 1], ref, torch.bfloat16, f"multi-token decode B16 b={b} L={L}")
+    del kc
 
 
 def test_stack_decode_layers_full_size_sampled():

@@ -339,6 +339,48 @@ def test_decode_from_cache_equals_prefill_row(kind):
         assert np.allclose(got, full[:, t], atol=1e-13)
 
 
+@pytest.mark.parametrize("group", [8, 2])
+def test_multi_token_decode_equals_the_prefill_rows(group):
+    """Several new tokens at once: token j is the prefill row at its position,
+    over a cache built by a prefill of the older tokens plus appends."""
+    d = 32
+    lay = layer(hq=2 * group, hkv=2, d=d, kv_shared=True, theta=1e6, p=0.25)
+    B, S, T = 2, 13, 3
+    q = RNG.normal(size=(B, S, lay.n_q_heads, d))
+    k = RNG.normal(size=(B, S, lay.n_kv_heads, d))
+    v = None
+    g_q = RNG.normal(1, 0.1, size=d)
+    g_k = RNG.normal(1, 0.1, size=d)
+    full = O.prefill(lay, q, k, v, g_q, g_k)
+    kc, vc = O.expected_caches_after_prefill(lay, k[:, :S - T], None if v is None else v[:, :S - T], g_k, S)
+    for t in range(S - T, S):
+        kc, vc = O.expected_caches_after_append(lay, kc, vc, k[:, t], None if v is None else v[:, t], g_k,
+                                                np.full(B, t))
+    got = O.decode_multi_from_cache(lay, q[:, S - T:], g_q, kc, vc, np.full(B, S))
+    assert np.allclose(got, full[:, S - T:], atol=1e-13)
+    # one token is the single-token decode
+    one = O.decode_multi_from_cache(lay, q[:, S - 1:], g_q, kc, vc, np.full(B, S))
+    assert np.allclose(one[:, 0], O.decode_from_cache(lay, q[:, S - 1], g_q, kc, vc, np.full(B, S)), atol=1e-13)
+
+
+def test_multi_token_decode_masks_the_later_new_tokens():
+    """Token 0 of two new tokens must not see the second token's key: changing
+    that key leaves token 0's output bit-identical and changes token 1's."""
+    d = 8
+    lay = layer(hq=2, hkv=1, d=d, kv_shared=True, theta=1e6, p=0.25)
+    q = RNG.normal(size=(1, 2, 2, d))
+    kc = RNG.normal(size=(1, 1, 6, d))
+    g = np.ones(d)
+    a = O.decode_multi_from_cache(lay, q, g, kc, None, np.array([6]))
+    kc2 = kc.copy()
+    kc2[0, 0, 5] += 1.0                               # the key of the second new token (position 5)
+    b = O.decode_multi_from_cache(lay, q, g, kc2, None, np.array([6]))
+    assert np.array_equal(a[:, 0], b[:, 0]) and not np.allclose(a[:, 1], b[:, 1])
+    with pytest.raises(ValueError):      # windowed and separate-V layers are not defined here
+        O.decode_multi_from_cache(layer(hq=2, hkv=1, d=d, window=3, theta=1e4, p=1.0), q, g, kc, kc,
+                                  np.array([6]))
+
+
 def test_global_cache_holds_one_unrotated_normalised_tensor():
     lay = layer(hq=8, hkv=1, d=16, kv_shared=True, theta=1e6, p=0.25)
     k = RNG.normal(size=(1, 5, 1, 16))
