@@ -9,8 +9,9 @@ one gemma_attn_prefill call (RoPE table + key/value prep + attention) on the
 32K global-layer prefill.  Reported beside it: the global decode (one
 gemma_attn_decode call on 16 sequences with lengths drawn from [4096, 131072],
 and kv_append on its own), the local-layer prefill (B=4, S=32K, window 1024)
-and one decode step of a 6-layer stack (5 local + 1 global layer, B=32, 64K
-context, kv_append then decode per layer).
+one decode step of a 6-layer stack (5 local + 1 global layer, B=32, 64K
+context, kv_append then decode per layer) and the global decode with two new
+tokens per sequence (multi-token decode).
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 """
 
@@ -70,6 +71,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-local", action="store_true", help="skip the local-layer prefill leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 6-layer stack decode leg")
+    ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
@@ -202,6 +204,50 @@ def bench_local_prefill(args, torch, api, W):
                      "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn / MI355X_BF16_DENSE_TFLOPS, 4),
                      "traffic": measured_traffic("local_prefill_attn"), "avg_ms": round(attn_ms, 4)},
+    }
+
+
+def bench_multi_decode(args, torch, api, W, q_len=2):
+    """Global K=V decode workload (B=16, contexts up to 128K) with q_len new tokens per sequence."""
+    wl = W.CONFIGS["global_decode"]
+    shape = wl.layer
+    dev = torch.device("cuda", 0)
+    lens = wl.lengths()
+    B, cap, D = wl.batch, wl.cache_cap(), shape.head_dim
+    kc = W.normal((B, shape.n_kv_heads, cap, D), wl.seed, "k_cache", torch.bfloat16, dev)
+    q = W.normal((B, q_len, shape.n_q_heads, D), wl.seed, "q_dec", torch.bfloat16, dev)
+    g_q = W.gains(D, wl.seed, "g_q", False, torch.bfloat16, dev)
+    lay = api.Layer.from_shape(shape, torch.bfloat16)
+    seq = lens.to(dev)
+    maxlen = int(lens.max())
+    out = torch.empty_like(q)
+    ws = api.workspace(api.gemma_attn_decode_multi_workspace_size(lay, B, q_len, maxlen), dev)
+
+    def step():
+        api.gemma_attn_decode_multi(lay, q, g_q, kc, None, seq, maxlen, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    sec = timed(step, args.decode_steps, 0, torch)
+    api.profile_enable(False)
+    split_ms, n_split = api.profile_read("decode_splitk")
+    api.profile_reset()
+    nbytes = wl.kv_bytes(lens)
+    del kc
+    torch.cuda.empty_cache()
+    gbs = nbytes / sec / 1e9
+    split_ms /= max(n_split, 1)
+    return {
+        "workload": f"global K=V layer, {q_len} new tokens per sequence (multi-token decode): B=16, "
+                    "context ~ U[4096,131072] (seed 0), 32q/4kv, d=512",
+        "q_len": q_len, "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(sec * 1e3, 4),
+        "tokens_per_s": round(B * q_len / sec, 1), "kv_bytes": nbytes,
+        "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V>", "bound": "hbm",
+                     "achieved": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4), "avg_ms": round(split_ms, 4)},
     }
 
 
@@ -346,6 +392,8 @@ def main():
                          "avg_ms": round(dec["split_ms"], 4), "merge_avg_ms": round(dec["merge_ms"], 4)},
             "kv_append_avg_ms": round(dec["append_ms"], 4),
         }
+    if not args.no_multi:
+        line["multi_token_decode"] = bench_multi_decode(args, torch, api, W)
     if not args.no_local:
         line["local_prefill"] = bench_local_prefill(args, torch, api, W)
     if not args.no_stack:
