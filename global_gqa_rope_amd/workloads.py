@@ -47,6 +47,11 @@ class LayerShape:
 GLOBAL_LAYER = LayerShape(32, 4, 512, 0, True, 1e6, 0.25)
 LOCAL_LAYER = LayerShape(32, 16, 256, 1024, False, 1e4, 1.0)
 TINY_GLOBAL = LayerShape(8, 1, 512, 0, True, 1e6, 0.25)
+# The smaller on-device models' layer types: 512-token windows, and global
+# layers with a separate V cache (no K=V).  Head counts are assumptions of the
+# same kind as the workloads above (8 query heads, 2 KV heads).
+E_LOCAL_LAYER = LayerShape(8, 2, 256, 512, False, 1e4, 1.0)
+E_GLOBAL_LAYER = LayerShape(8, 2, 512, 0, False, 1e6, 0.25)
 TINY_LOCAL = LayerShape(4, 2, 256, 64, False, 1e4, 1.0)
 
 

@@ -215,8 +215,13 @@ def expected_caches_after_prefill(layer: OracleLayer, k, v, g_k, cache_cap: int)
             raise ValueError("prompt longer than the cache")
         kc[:, :, :S] = k_hat.transpose(0, 2, 1, 3)
         return kc, None
-    if cache_cap != layer.window:
+    # Separate V: keys stored rotated.  Windowed layers keep a ring of W
+    # slots (slot = position mod W); global ones every position (slot =
+    # position), as the E2B/E4B global layers without K=V need.
+    if layer.window > 0 and cache_cap != layer.window:
         raise ValueError("a local cache has exactly W slots")
+    if layer.window == 0 and S > cache_cap:
+        raise ValueError("prompt longer than the cache")
     positions = np.arange(S)
     k_rot = rotate(k_hat, positions[None, :, None], layer.rope_theta,
                    layer.rope_fraction)
@@ -249,9 +254,10 @@ def decode_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
     """One decode step per sequence: q [B,Hq,d] raw, query position L_b - 1.
 
     ``seq_lens[b]`` counts the valid keys including the new token.  Global
-    layers read slots 0..L_b-1 of the K=V cache (slot j = position j) and rotate
-    them on the fly; local layers read the min(L_b, W) filled ring slots, whose
-    keys are stored already rotated.  Returns out [len(batches), Hq, d].
+    layers read slots 0..L_b-1 (slot j = position j): K=V caches are rotated on
+    the fly, separate-V caches hold rotated keys.  Local layers read the
+    min(L_b, W) filled ring slots, whose keys are stored already rotated.
+    Returns out [len(batches), Hq, d].
     """
     G = layer.group
     batches = range(q.shape[0]) if batches is None else batches
@@ -270,6 +276,12 @@ def decode_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
                 for h in range(c * G, (c + 1) * G):
                     rows[h] = masked_softmax_attention(q_rot[h:h + 1], qpos, k_rot,
                                                        keys, kpos, layer.scale, 0)[0]
+        elif layer.window == 0:
+            # global layer with a separate V: slot = position, keys stored rotated
+            kpos = np.arange(L)
+            for h in range(layer.n_q_heads):
+                rows[h] = masked_softmax_attention(
+                    q_rot[h:h + 1], qpos, k_cache[b, h // G, :L], v_cache[b, h // G, :L], kpos, layer.scale, 0)[0]
         else:
             n = min(L, layer.window)
             # Slot s holds the latest position congruent to s mod W; all of the

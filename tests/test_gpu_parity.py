@@ -91,6 +91,9 @@ PREFILL_CASES = [
     ("local_G1_W100", W.replace(W.LOCAL_LAYER, n_q_heads=16, window=100), 1, 257),
     # 12 workgroups: the XCD-aware order of windowed layers with a grid that 8 does not divide
     ("local_Hkv3_W64", W.replace(W.LOCAL_LAYER, n_q_heads=6, n_kv_heads=3, window=64), 1, 200),
+    # the smaller models' layer types: global without K=V (separate V cache), 512-token window
+    ("e_global_separate_v", W.E_GLOBAL_LAYER, 2, 300),
+    ("e_local_W512", W.E_LOCAL_LAYER, 1, 1100),
 ]
 
 
@@ -148,17 +151,40 @@ def _decode_case(shape, lens, dtype, seed, cap=None):
     return q, g_q, kc, vc, seq, out
 
 
+DECODE_SHAPES = {"global": W.GLOBAL_LAYER, "local": W.LOCAL_LAYER, "e_global": W.E_GLOBAL_LAYER,
+                 "e_local": W.E_LOCAL_LAYER}
+
+
 @pytest.mark.parametrize("kind,lens", [
     ("global", [1, 17, 1024, 1025, 2600]),
     ("global", [4097, 3000]),
     ("local", [5, 1024, 1025, 5000]),
+    ("e_global", [1, 17, 1024, 1025, 2600]),
+    ("e_local", [5, 512, 513, 3000]),
 ])
 def test_decode_bf16(kind, lens):
-    shape = W.GLOBAL_LAYER if kind == "global" else W.LOCAL_LAYER
+    shape = DECODE_SHAPES[kind]
     q, g_q, kc, vc, seq, out = _decode_case(shape, lens, torch.bfloat16, seed=7)
     ref = O.decode_from_cache(oracle_layer(shape), to64(q), to64(g_q), to64(kc),
                               None if vc is None else to64(vc), seq.numpy())
     assert_close(out, ref, torch.bfloat16, f"{kind} decode {lens}")
+
+
+def test_layers_sharing_one_cache():
+    """Cross-layer cache sharing (the smaller models reuse a layer's cache in
+    later layers): a layer that only reads another layer's cache, with its own
+    queries and gains, is attention over that cache."""
+    shape = W.E_LOCAL_LAYER
+    x, xd, out, kc, vc = _prefill_case(shape, 1, 700, torch.bfloat16, False, seed=17)   # the owner fills the ring
+    dev = device()
+    D = shape.head_dim
+    q2 = W.normal((1, shape.n_q_heads, D), 23, "q_dec", torch.bfloat16, dev)
+    g2 = W.gains(D, 23, "g_q", False, torch.bfloat16, dev)
+    seq = torch.tensor([700], dtype=torch.int32, device=dev)
+    got = api.gemma_attn_decode(api_layer(shape, torch.bfloat16), q2, g2, kc, vc, seq, 700)
+    torch.cuda.synchronize()
+    ref = O.decode_from_cache(oracle_layer(shape), to64(q2), to64(g2), to64(kc), to64(vc), np.array([700]))
+    assert_close(got, ref, torch.bfloat16, "reader layer on the owner's cache")
 
 
 def test_decode_invalid_lengths_write_nan_rows():

@@ -313,11 +313,13 @@ def test_softmax_scale_default_is_inverse_sqrt_head_dim():
 
 # --------------------------------------------------- decode and caches ----
 
-@pytest.mark.parametrize("kind", ["global", "local"])
+@pytest.mark.parametrize("kind", ["global", "global_separate_v", "local"])
 def test_decode_from_cache_equals_prefill_row(kind):
     d = 32
     if kind == "global":
         lay = layer(hq=8, hkv=1, d=d, kv_shared=True, theta=1e6, p=0.25)
+    elif kind == "global_separate_v":         # E2B/E4B global layers: no K=V
+        lay = layer(hq=8, hkv=2, d=d, kv_shared=False, theta=1e6, p=0.25)
     else:
         lay = layer(hq=4, hkv=2, d=d, window=6, theta=1e4, p=1.0)
     B, T = 2, 15                      # T > W exercises the ring wrap
@@ -328,7 +330,7 @@ def test_decode_from_cache_equals_prefill_row(kind):
     g_q = RNG.normal(1, 0.1, size=d)
     g_k = RNG.normal(1, 0.1, size=d)
     full = O.prefill(lay, q, k, v, g_q, g_k)
-    cap = T if lay.kv_shared else lay.window
+    cap = lay.window if lay.window else T
     kc, vc = O.expected_caches_after_prefill(lay, k[:, :T - 4],
                                              None if v is None else v[:, :T - 4], g_k, cap)
     for t in range(T - 4, T):
