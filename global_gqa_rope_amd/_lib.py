@@ -41,6 +41,8 @@ SIGNATURES = {
     "gemma_attn_prefill_workspace_size": (_Z, [_LP, _I, _I]),
     "gemma_attn_prefill": (_I, [_LP, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
     "kv_append": (_I, [_LP, _I, _P, _P, _P, _P, _P, _P, _I, _P]),
+    "gemma_attn_prefill_chunk_workspace_size": (_Z, [_LP, _I, _I, _I]),
+    "gemma_attn_prefill_chunk": (_I, [_LP, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
     "gemma_attn_decode_workspace_size": (_Z, [_LP, _I, _I]),
     "gemma_attn_decode": (_I, [_LP, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "gemma_attn_decode_multi_workspace_size": (_Z, [_LP, _I, _I, _I]),

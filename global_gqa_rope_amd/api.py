@@ -114,6 +114,31 @@ def gemma_attn_prefill(layer: Layer, q, k, v, q_gain, k_gain, k_cache=None, v_ca
     return out
 
 
+def gemma_attn_prefill_chunk_workspace_size(layer: Layer, batch: int, start: int, chunk: int) -> int:
+    return int(_lib.load().gemma_attn_prefill_chunk_workspace_size(ctypes.byref(layer.struct()), batch, start,
+                                                                     chunk))
+
+
+def gemma_attn_prefill_chunk(layer: Layer, start: int, q, k, q_gain, k_gain, k_cache, out=None, ws=None,
+                             stream=None) -> torch.Tensor:
+    """Positions start .. start + chunk - 1 against k_cache slots 0 .. start - 1 (global K=V layers)."""
+    B, T, Hq, d = q.shape
+    Hkv = layer.n_kv_heads
+    cap = k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = workspace(gemma_attn_prefill_chunk_workspace_size(layer, B, start, T), q.device)
+    st = _lib.load().gemma_attn_prefill_chunk(
+        ctypes.byref(layer.struct()), B, int(start), T, _ptr(q, "q", layer, (B, T, Hq, d)),
+        _ptr(k, "k", layer, (B, T, Hkv, d)), _ptr(q_gain, "q_gain", layer, (d,)),
+        _ptr(k_gain, "k_gain", layer, (d,)), _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d)), cap,
+        _ptr(out, "out", layer, (B, T, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8), ws.numel(),
+        _stream(stream))
+    _lib.check(st)
+    return out
+
+
 def kv_append(layer: Layer, k_new, v_new, k_gain, positions, k_cache, v_cache=None,
               stream=None) -> None:
     B, Hkv, d = k_new.shape

@@ -270,17 +270,27 @@ size_t gemma_attn_decode_multi_workspace_size(const ga_layer* layer, int32_t bat
   return decode_bytes(layer, dv, batch, q_len, max_seq_len);
 }
 
-ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_len, const void* q,
-                             const void* k, const void* v, const void* q_gain, const void* k_gain,
-                             void* k_cache, void* v_cache, int32_t cache_cap, void* out,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+// Prefill of positions start .. start + seq_len - 1 of every sequence.  start
+// > 0 (global K=V layers): positions 0 .. start - 1 are in k_cache already and
+// are read back into the workspace rows.
+static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t start, int32_t seq_len, const void* q,
+                              const void* k, const void* v, const void* q_gain, const void* k_gain, void* k_cache,
+                              void* v_cache, int32_t cache_cap, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   Derived dv;
   ga_status st = check_layer(layer, &dv);
   if (st != GA_OK) return st;
-  if (batch < 0 || seq_len < 0) return fail(GA_EINVAL, "batch and seq_len must be >= 0");
-  if (seq_len > (1 << 22)) return fail(GA_EUNSUPPORTED, "seq_len above 4M positions");
-  if (static_cast<int64_t>(seq_len + ga::kPrepTile) * layer->head_dim * dv.elem > INT32_MAX)
-    return fail(GA_EUNSUPPORTED, "seq_len %d: one head's key tiles must stay under 2 GiB", seq_len);
+  if (batch < 0 || seq_len < 0 || start < 0) return fail(GA_EINVAL, "batch, start and seq_len must be >= 0");
+  const int64_t total = static_cast<int64_t>(start) + seq_len;
+  if (total > (1 << 22)) return fail(GA_EUNSUPPORTED, "seq_len above 4M positions");
+  if ((total + ga::kPrepTile) * layer->head_dim * dv.elem > INT32_MAX)
+    return fail(GA_EUNSUPPORTED, "seq_len %lld: one head's key tiles must stay under 2 GiB",
+                static_cast<long long>(total));
+  if (start > 0) {
+    if (!layer->kv_shared || layer->window > 0)
+      return fail(GA_EUNSUPPORTED, "a prefill chunk after cached positions is built for global K=V layers only");
+    if (!k_cache) return fail(GA_EINVAL, "a prefill chunk after cached positions needs the k_cache holding them");
+  }
   if (batch == 0 || seq_len == 0) return GA_OK;
   if (!q || !k || !q_gain || !k_gain || !out) return fail(GA_EINVAL, "q, k, q_gain, k_gain and out must be non-NULL");
   if (layer->kv_shared && v) return fail(GA_EINVAL, "K=V layer: v must be NULL (keys are the values)");
@@ -290,9 +300,9 @@ ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_l
                         static_cast<const void*>(out)})
     if (reinterpret_cast<uintptr_t>(t) % 16)
       return fail(GA_EINVAL, "q, k, v, the gains, the caches and out must be 16-byte aligned");
-  st = check_caches(layer, k_cache, v_cache, cache_cap, true, seq_len);
+  st = check_caches(layer, k_cache, v_cache, cache_cap, true, static_cast<int32_t>(total));
   if (st != GA_OK) return st;
-  const PrefillLayout lay = prefill_layout(layer, dv, batch, seq_len);
+  const PrefillLayout lay = prefill_layout(layer, dv, batch, static_cast<int32_t>(total));
   st = check_workspace(workspace, workspace_bytes, lay.total);
   if (st != GA_OK) return st;
 
@@ -308,6 +318,7 @@ ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_l
       pa.k_cache = k_cache; pa.v_cache = v_cache; pa.ws_k = ws + lay.ws_k; pa.ws_v = ws + lay.ws_v; pa.kw = lay.kw;
       pa.seq_len = seq_len; pa.seq_pad = lay.seq_pad; pa.n_kv_heads = layer->n_kv_heads; pa.n_rot = dv.n_rot;
       pa.window = layer->window; pa.kv_shared = layer->kv_shared; pa.cache_cap = cache_cap; pa.eps = layer->norm_eps;
+      pa.pos0 = start;
       st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "prefill prep launch");
     }
   }
@@ -317,10 +328,35 @@ ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_l
   fa.q = q; fa.q_gain = q_gain; fa.rope_table = ws + lay.table; fa.ws_k = ws + lay.ws_k; fa.ws_v = ws + lay.ws_v;
   fa.out = out; fa.seq_len = seq_len; fa.seq_pad = lay.seq_pad; fa.n_q_heads = layer->n_q_heads;
   fa.n_kv_heads = layer->n_kv_heads; fa.n_rot = dv.n_rot; fa.window = layer->window; fa.eps = layer->norm_eps;
+  fa.q_pos0 = start;
   fa.qk_scale_log2 = dv.scale * 1.4426950408889634f;
   ProfScope ps(s, 0);
   return hip_status(ga::launch_prefill_attn(fa, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch, s),
                     "prefill attention launch");
+}
+
+ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_len, const void* q,
+                             const void* k, const void* v, const void* q_gain, const void* k_gain,
+                             void* k_cache, void* v_cache, int32_t cache_cap, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(layer, batch, 0, seq_len, q, k, v, q_gain, k_gain, k_cache, v_cache, cache_cap, out, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t gemma_attn_prefill_chunk_workspace_size(const ga_layer* layer, int32_t batch, int32_t start, int32_t chunk) {
+  Derived dv;
+  if (check_layer(layer, &dv) != GA_OK || batch < 0 || start < 0 || chunk < 0) return 0;
+  const int64_t total = static_cast<int64_t>(start) + chunk;
+  if (total > (1 << 22)) return 0;
+  return prefill_layout(layer, dv, batch, static_cast<int32_t>(total)).total;
+}
+
+ga_status gemma_attn_prefill_chunk(const ga_layer* layer, int32_t batch, int32_t start, int32_t chunk,
+                                   const void* q, const void* k, const void* q_gain, const void* k_gain,
+                                   void* k_cache, int32_t cache_cap, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return prefill_impl(layer, batch, start, chunk, q, k, nullptr, q_gain, k_gain, k_cache, nullptr, cache_cap, out,
+                      workspace, workspace_bytes, stream);
 }
 
 ga_status kv_append(const ga_layer* layer, int32_t batch, const void* k_new, const void* v_new,

@@ -32,6 +32,7 @@ struct PrepArgs {
   void* ws_k;              // [B][Hkv][seq_pad][kw] rotated normalised keys
   void* ws_v;              // [B][Hkv][seq_pad][d] value rows
   int seq_len, seq_pad, n_kv_heads, n_rot, window, kv_shared, cache_cap, kw;
+  int pos0;                // position of k's first row; rows 0 .. pos0-1 come from the K=V cache
   float eps;
 };
 
@@ -55,6 +56,7 @@ struct PrefillArgs {
   const void* ws_v;
   void* out;
   int seq_len, seq_pad, n_q_heads, n_kv_heads, n_rot, window;
+  int q_pos0;              // position of q's (and out's) first row; keys from position 0
   float eps;
   float qk_scale_log2;     // softmax scale * log2(e), folded into q
 };

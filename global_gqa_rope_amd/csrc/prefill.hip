@@ -551,13 +551,16 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, h = lane >> 5;                     // row of this lane, half of the slice
-  const int p0 = qb * C::QB;
+  // Query rows are positions q_pos0 .. q_pos0 + seq_len - 1 (q_pos0 > 0: a
+  // later chunk of a prompt whose earlier keys are in the workspace rows too).
+  const int p0 = a.q_pos0 + qb * C::QB;
   const int pos = p0 + wave * C::PW + m / G;                  // query position of row m
+  const int lpos = pos - a.q_pos0;                            // its row in q and out
   const int qh = kvh * G + (m % G);                           // query head of row m
-  const bool row_valid = pos < a.seq_len;
+  const bool row_valid = lpos < a.seq_len;
 
   // ---- tile stream setup: start the first kStages - 1 copies -------------------
-  const int p_last = min(p0 + C::QB, a.seq_len) - 1;
+  const int p_last = min(p0 + C::QB, a.q_pos0 + a.seq_len) - 1;
   const int kt_lo = a.window > 0 ? max(0, p0 - a.window + 1) / C::KT : 0;
   const int kt_hi = p_last / C::KT + 1;
   const int64_t head = static_cast<int64_t>(b) * a.n_kv_heads + kvh;
@@ -578,7 +581,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   constexpr bool kQRegs = sizeof(T) == 2;
   Frag8<T> qf[kQRegs ? C::kQSteps : 1];
   const T* __restrict__ qrow = static_cast<const T*>(a.q) +
-      ((static_cast<int64_t>(b) * a.seq_len + (row_valid ? pos : 0)) * a.n_q_heads + qh) * D;
+      ((static_cast<int64_t>(b) * a.seq_len + (row_valid ? lpos : 0)) * a.n_q_heads + qh) * D;
   const T* __restrict__ gq = static_cast<const T*>(a.q_gain);
   const f32x2* __restrict__ qtable = static_cast<const f32x2*>(a.rope_table) +
                                      static_cast<int64_t>(row_valid ? pos : 0) * a.n_rot;
@@ -744,7 +747,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const float l = sum_halves(st.l_part);
   const float inv = 1.0f / l;
   T* __restrict__ out = static_cast<T*>(a.out) +
-      ((static_cast<int64_t>(b) * a.seq_len + (row_valid ? pos : 0)) * a.n_q_heads + qh) * D;
+      ((static_cast<int64_t>(b) * a.seq_len + (row_valid ? lpos : 0)) * a.n_q_heads + qh) * D;
   if constexpr (sizeof(T) == 2) {
     // Lanes m and m + 32 hold the two 4-dim halves of each 8-dim run of row
     // m.  One row swap per pair of runs hands each lane a whole run (lane m

@@ -21,7 +21,10 @@ __global__ void rope_table_kernel(f32x2* __restrict__ table, int n_pos, int n_ro
 // Thread t owns key row r = t / 8 of the tile and the 8-element chunks
 // i * 8 + t % 8 of that row, so eight neighbouring lanes cover 64 contiguous
 // elements of one row.  Every global access is a 16-byte vector, and all
-// loads of a thread are issued before the first use.
+// loads of a thread are issued before the first use.  Positions pos0 ..
+// pos0 + seq_len - 1 are k's rows; on K=V layers positions below pos0 are
+// already in the cache (a later chunk of a prompt) and are read back from it,
+// normalised and unrotated, into the key and value rows.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   constexpr int kChunks = D / 8;             // 8-element chunks per row
@@ -32,11 +35,13 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   const int t = threadIdx.x;
   const int r = t >> 3, c8 = t & 7;
   const int pos = tile * kPrepTile + r;
-  const bool valid = pos < a.seq_len;
-  // padding positions read the last real row (then zeroed) so no load leaves the tensor
-  const int src_pos = valid ? pos : a.seq_len - 1;
+  const bool valid = pos >= a.pos0 && pos < a.pos0 + a.seq_len;   // one of k's rows
+  const bool cached = pos < a.pos0;                                // already in the K=V cache
+  // other positions read k's last row (then zeroed) so no load leaves the tensor
+  const int src_pos = valid ? pos - a.pos0 : a.seq_len - 1;
   const int64_t src_row = ((static_cast<int64_t>(b) * a.seq_len + src_pos) * a.n_kv_heads + h) * D;
   const bool has_v = !a.kv_shared;
+  const int64_t head_base = (static_cast<int64_t>(b) * a.n_kv_heads + h);
 
   const T* __restrict__ k = static_cast<const T*>(a.k);
   const T* __restrict__ v = static_cast<const T*>(a.v);
@@ -45,10 +50,11 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
 
   vec8 kin[kMine], vin[kMine], gin[kMine];
   f32x2 cs[kMine][4];
+  const T* __restrict__ cache_row = static_cast<const T*>(a.k_cache) + (head_base * a.cache_cap + pos) * D;
 #pragma unroll
   for (int i = 0; i < kMine; ++i) {
     const int d0 = (i * 8 + c8) * 8;
-    kin[i] = *reinterpret_cast<const vec8*>(k + src_row + d0);
+    kin[i] = *reinterpret_cast<const vec8*>((cached ? cache_row : k + src_row) + d0);
     gin[i] = *reinterpret_cast<const vec8*>(gk + d0);
     if (has_v) vin[i] = *reinterpret_cast<const vec8*>(v + src_row + d0);
   }
@@ -69,19 +75,20 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   for (int i = 0; i < kMine; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      x[i][j] = valid ? to_f32(kin[i][j]) : 0.f;
+      x[i][j] = (valid || cached) ? to_f32(kin[i][j]) : 0.f;
       ss += x[i][j] * x[i][j];
     }
   ss += wave_xor(ss, 1);
   ss += wave_xor(ss, 2);
   ss += wave_xor(ss, 4);
   const float rstd = 1.0f / sqrtf(ss / D + a.eps);
+  if (!cached) {   // cached rows are normalised already
 #pragma unroll
-  for (int i = 0; i < kMine; ++i)
+    for (int i = 0; i < kMine; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[i][j] = x[i][j] * rstd * to_f32(gin[i][j]);
+      for (int j = 0; j < 8; ++j) x[i][j] = x[i][j] * rstd * to_f32(gin[i][j]);
+  }
 
-  const int64_t head_base = (static_cast<int64_t>(b) * a.n_kv_heads + h);
   const int64_t row = head_base * a.seq_pad + pos;          // row in ws_k / ws_v
   T* __restrict__ kc = static_cast<T*>(a.k_cache);
   T* __restrict__ vc = static_cast<T*>(a.v_cache);

@@ -134,6 +134,32 @@ ga_status kv_append(const ga_layer* layer, int32_t batch,
                     int32_t cache_cap, void* stream);
 
 /*
+ * Prefill of a later chunk of a prompt against the positions already cached
+ * (global K=V layers): positions start .. start + chunk - 1 of each sequence
+ * attend causally to positions 0 .. their own, where k_cache slots
+ * 0 .. start - 1 hold the earlier positions (as a prefill or kv_append wrote
+ * them).  The chunk's keys are normalised into slots start .. start + chunk - 1.
+ * Each output row is the row a prefill of the whole prompt would give; this is
+ * the longer form of checking many new tokens at once (see
+ * gemma_attn_decode_multi).
+ *
+ *   q [B, chunk, Hq, d], k [B, chunk, Hkv, d] raw; out [B, chunk, Hq, d]
+ *   k_cache [B, Hkv, cache_cap, d], cache_cap >= start + chunk
+ *   workspace >= gemma_attn_prefill_chunk_workspace_size() bytes, 256-byte
+ *   aligned (the workspace of a prefill of start + chunk positions).
+ * start = 0 is gemma_attn_prefill with a cache.  GA_EUNSUPPORTED for start > 0
+ * on a layer other than a global K=V one; other errors as for
+ * gemma_attn_prefill.
+ */
+size_t gemma_attn_prefill_chunk_workspace_size(const ga_layer* layer, int32_t batch,
+                                               int32_t start, int32_t chunk);
+ga_status gemma_attn_prefill_chunk(const ga_layer* layer, int32_t batch, int32_t start,
+                                   int32_t chunk, const void* q, const void* k,
+                                   const void* q_gain, const void* k_gain, void* k_cache,
+                                   int32_t cache_cap, void* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of scratch gemma_attn_decode needs: per-sequence tile offsets and the
  * split-K partial results (one per wave and visited segment).  Depends on the
  * layer, batch and max_seq_len only, never on the device.

@@ -131,6 +131,23 @@ def test_multi_token_decode_validation(lib):
     assert wsz(g2, 3, 8, 1000) == decode_ws(3, 4, 16, 512, 1000)
 
 
+def test_prefill_chunk_validation(lib):
+    g = L()
+    loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
+    ch = lambda **kw: lib.gemma_attn_prefill_chunk(
+        ctypes.byref(kw.get("layer", g)), 1, kw.get("start", 64), kw.get("chunk", 16), FAKE, FAKE, FAKE, FAKE,
+        kw.get("kc", FAKE), kw.get("cap", 4096), FAKE, FAKE, 1 << 40, None)
+    assert ch(layer=loc, cap=1024) == 2                         # later chunks: global K=V layers only
+    assert ch(kc=None) == 1                                     # the cached positions live in k_cache
+    assert ch(cap=79) == 1                                      # cap >= start + chunk
+    assert ch(start=-1) == 1
+    assert ch(chunk=0) == 0                                     # no-op
+    wsz = lambda start, chunk: lib.gemma_attn_prefill_chunk_workspace_size(ctypes.byref(g), 2, start, chunk)
+    # the workspace of a prefill of start + chunk positions
+    assert wsz(1000, 37) == lib.gemma_attn_prefill_workspace_size(ctypes.byref(g), 2, 1037)
+    assert wsz(0, 512) == lib.gemma_attn_prefill_workspace_size(ctypes.byref(g), 2, 512)
+
+
 def test_workspace_sizes_follow_the_layout(lib):
     g = L()
     # table (S_pad * 64 pairs * 8 B) + key rows [B,Hkv,S_pad,128] (the rotated

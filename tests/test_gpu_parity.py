@@ -254,6 +254,47 @@ def test_multi_token_decode_short_sequences_write_nan_rows():
     assert_close(out[1:], ref, torch.bfloat16, "valid sequences next to a short one")
 
 
+# ---- a later chunk of a prompt against the cached positions (global K=V) ------------
+
+def _chunked(shape, B, S, cuts, seed):
+    """Prefill positions 0 .. S-1 as consecutive chunks [cuts[i], cuts[i+1])."""
+    dev = device()
+    wl = W.PrefillWorkload("chunks", shape, B, S, torch.bfloat16, False, seed)
+    x = wl.draw("cpu")
+    xd = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    lay = api_layer(shape, torch.bfloat16)
+    kc = torch.full((B, shape.n_kv_heads, S, shape.head_dim), float("nan"), dtype=torch.bfloat16, device=dev)
+    out = torch.full_like(xd["q"], float("nan"))
+    bounds = [0] + list(cuts) + [S]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        o = api.gemma_attn_prefill_chunk(lay, a, xd["q"][:, a:b].contiguous(), xd["k"][:, a:b].contiguous(),
+                                         xd["g_q"], xd["g_k"], kc)
+        out[:, a:b] = o
+    torch.cuda.synchronize()
+    return x, xd, out, kc
+
+
+@pytest.mark.parametrize("S,cuts", [(700, [300]), (300, [37, 107, 299]), (1100, [1024])])
+def test_prefill_in_chunks_equals_the_whole_prompt(S, cuts):
+    shape = W.GLOBAL_LAYER
+    x, xd, out, kc = _chunked(shape, 2, S, cuts, seed=31)
+    ol = oracle_layer(shape)
+    ref = O.prefill(ol, to64(x["q"]), to64(x["k"]), None, to64(x["g_q"]), to64(x["g_k"]))
+    assert_close(out, ref, torch.bfloat16, f"chunks {cuts} of {S}")
+    okc, _ = O.expected_caches_after_prefill(ol, to64(x["k"]), None, to64(x["g_k"]), S)
+    assert_close(kc, okc, torch.bfloat16, "cache after the chunks")
+
+
+def test_first_chunk_equals_prefill():
+    shape = W.GLOBAL_LAYER
+    x, xd, out, kc = _chunked(shape, 1, 333, [], seed=33)
+    lay = api_layer(shape, torch.bfloat16)
+    kc2 = torch.full_like(kc, float("nan"))
+    whole = api.gemma_attn_prefill(lay, xd["q"], xd["k"], None, xd["g_q"], xd["g_k"], kc2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), whole.cpu()) and torch.equal(kc.cpu(), kc2.cpu())
+
+
 def test_kv_append_ignores_out_of_range_positions():
     shape = W.GLOBAL_LAYER
     dev = device()
@@ -314,6 +355,26 @@ def _sampled_prefill(wl, rows, batches, what):
         assert_close(kc[b:b + 1, :, S - 8:], okc, torch.bfloat16, f"{what} cache slots")
     else:
         assert_close(kc[b:b + 1], okc, torch.bfloat16, f"{what} k ring")
+
+
+def test_global_prefill_32k_last_chunk_sampled_rows():
+    """The 32K global prefill as 28K positions, then a 4K chunk against them."""
+    wl = W.CONFIGS["global_prefill_32k"]
+    shape, S, start = wl.layer, wl.seq_len, 28672
+    dev = device()
+    x = wl.draw(dev)
+    lay = api_layer(shape, torch.bfloat16)
+    kc = torch.empty((1, shape.n_kv_heads, S, shape.head_dim), dtype=torch.bfloat16, device=dev)
+    api.gemma_attn_prefill(lay, x["q"][:, :start].contiguous(), x["k"][:, :start].contiguous(), None, x["g_q"],
+                           x["g_k"], kc)
+    out = api.gemma_attn_prefill_chunk(lay, start, x["q"][:, start:].contiguous(), x["k"][:, start:].contiguous(),
+                                       x["g_q"], x["g_k"], kc)
+    torch.cuda.synchronize()
+    rows = [start, start + 1, start + 1000, S - 1]
+    ref = O.prefill(oracle_layer(shape), to64(x["q"][:, torch.as_tensor(rows, device=dev)]), to64(x["k"]), None,
+                    to64(x["g_q"]), to64(x["g_k"]), rows=np.asarray(rows), q_at_rows=True)
+    got = out[:, torch.as_tensor([r - start for r in rows], device=dev)]
+    assert_close(got, ref, torch.bfloat16, f"last chunk rows {rows}")
 
 
 def test_global_prefill_32k_sampled_rows():
