@@ -10,8 +10,9 @@ one gemma_attn_prefill call (RoPE table + key/value prep + attention) on the
 gemma_attn_decode call on 16 sequences with lengths drawn from [4096, 131072],
 and kv_append on its own), the local-layer prefill (B=4, S=32K, window 1024)
 one decode step of a 6-layer stack (5 local + 1 global layer, B=32, 64K
-context, kv_append then decode per layer) and the global decode with two new
-tokens per sequence (multi-token decode).
+context, kv_append then decode per layer), the global decode with two new
+tokens per sequence (multi-token decode) and the last 4K positions of the 32K
+global prompt as a chunk against the 28K cached ones (chunked prefill).
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 """
 
@@ -72,6 +73,7 @@ def parse():
     ap.add_argument("--no-local", action="store_true", help="skip the local-layer prefill leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 6-layer stack decode leg")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode leg")
+    ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
@@ -204,6 +206,49 @@ def bench_local_prefill(args, torch, api, W):
                      "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn / MI355X_BF16_DENSE_TFLOPS, 4),
                      "traffic": measured_traffic("local_prefill_attn"), "avg_ms": round(attn_ms, 4)},
+    }
+
+
+def bench_prefill_chunk(args, torch, api, W, start=28672):
+    """The last 4K positions of the 32K global prompt as a chunk against the 28K cached ones."""
+    wl = W.CONFIGS["global_prefill_32k"]
+    shape, S = wl.layer, wl.seq_len
+    dev = torch.device("cuda", 0)
+    x = wl.draw(dev)
+    lay = api.Layer.from_shape(shape, torch.bfloat16)
+    kc = torch.empty((1, shape.n_kv_heads, S, shape.head_dim), dtype=torch.bfloat16, device=dev)
+    api.gemma_attn_prefill(lay, x["q"][:, :start].contiguous(), x["k"][:, :start].contiguous(), None, x["g_q"],
+                           x["g_k"], kc)
+    q, k = x["q"][:, start:].contiguous(), x["k"][:, start:].contiguous()
+    out = torch.empty_like(q)
+    ws = api.workspace(api.gemma_attn_prefill_chunk_workspace_size(lay, 1, start, S - start), dev)
+
+    def step():
+        api.gemma_attn_prefill_chunk(lay, start, q, k, x["g_q"], x["g_k"], kc, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    sec = timed(step, args.steps, 0, torch)
+    api.profile_enable(False)
+    attn_ms, n_attn = api.profile_read("prefill_attn")
+    prep_ms, n_prep = api.profile_read("prefill_prep")
+    api.profile_reset()
+    del x, kc, q, k, out, ws
+    torch.cuda.empty_cache()
+    flops = 4.0 * shape.n_q_heads * shape.head_dim * sum(range(start + 1, S + 1))
+    attn_ms /= max(n_attn, 1)
+    attn = flops / (attn_ms * 1e-3) / 1e12
+    return {
+        "workload": "global K=V layer, positions 28672..32767 of a 32K prompt as one chunk against the 28672 "
+                    "cached positions (chunked prefill), 32q/4kv, d=512",
+        "value": round(flops / sec / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(sec * 1e3, 3),
+        "flops_per_step": flops, "prep_avg_ms": round(prep_ms / max(n_prep, 1), 4),
+        "roofline": {"kernel": "prefill_attn_kernel<bf16,512,8>", "bound": "mfma", "achieved": round(attn, 2),
+                     "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn / MI355X_BF16_DENSE_TFLOPS, 4), "avg_ms": round(attn_ms, 4)},
     }
 
 
@@ -394,6 +439,8 @@ def main():
         }
     if not args.no_multi:
         line["multi_token_decode"] = bench_multi_decode(args, torch, api, W)
+    if not args.no_chunk:
+        line["prefill_chunk"] = bench_prefill_chunk(args, torch, api, W)
     if not args.no_local:
         line["local_prefill"] = bench_local_prefill(args, torch, api, W)
     if not args.no_stack:
