@@ -34,11 +34,13 @@ from .attention import (  # noqa: F401
     cache_bytes_per_token,
     decode_from_cache,
     decode_multi_from_cache,
+    dequantize_rows,
     expected_caches_after_append,
     expected_caches_after_prefill,
     masked_softmax_attention,
     prefill,
     qk_norm,
+    quantize_rows,
     rope_frequencies,
     rotate,
     rotated_pairs,

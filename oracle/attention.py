@@ -331,6 +331,30 @@ def decode_multi_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_le
     return np.stack(out)
 
 
+# --- int8 K=V cache ------------------------------------------------------------
+# The pages' 32K memory table counts the KV cache in int8 (table "显存占用（32k
+# 上下文，文本 only，int8 KV cache）" of "Gemma 4 技术报告：开源全模态密集 + MoE 模型家族，
+# 长上下文与端侧高效是本代核心").  They do not say how values map to int8; the
+# reading taken here is symmetric scaling per cached row (one position of one
+# KV head): codes c_i = round-half-even(x_i / s) with s = max_i |x_i| / 127,
+# standing for c_i * s.  The code is an integer decided by floating point, so
+# it is computed in float32, the precision the kernels use.
+
+def quantize_rows(x):
+    """int8 codes [..., d] and float32 scales [...] of rows x[..., d]."""
+    x32 = np.asarray(x, dtype=np.float32)
+    s = np.max(np.abs(x32), axis=-1) / np.float32(127.0)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    c = np.rint(x32 / safe[..., None])
+    c = np.where(s[..., None] > 0, np.clip(c, -127, 127), 0.0)
+    return c.astype(np.int8), s.astype(np.float32)
+
+
+def dequantize_rows(codes, scales) -> np.ndarray:
+    """The rows int8 codes and their scales stand for: c_i * s."""
+    return np.asarray(codes, dtype=np.float64) * _f64(scales)[..., None]
+
+
 def cache_bytes_per_token(head_dim: int, fraction: float, layout: str,
                           bytes_per_elem: float = 1.0) -> float:
     """Bytes one KV head caches per token under three global-layer layouts.

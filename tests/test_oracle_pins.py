@@ -383,6 +383,22 @@ def test_multi_token_decode_masks_the_later_new_tokens():
                                   np.array([6]))
 
 
+def test_int8_rows_hand_values_and_bounds():
+    x = np.array([[1.27, -0.635, 0.0, 0.005], [0.0, 0.0, 0.0, 0.0]])
+    c, s = O.quantize_rows(x)
+    assert s.dtype == np.float32 and c.dtype == np.int8
+    assert np.isclose(s[0], 0.01) and s[1] == 0
+    assert c[0].tolist() == [127, -64, 0, 0]                 # -63.5 and 0.5 round half to even
+    assert (c[1] == 0).all() and (O.dequantize_rows(c, s)[1] == 0).all()
+    rows = RNG.normal(size=(64, 512))
+    c, s = O.quantize_rows(rows)
+    assert (np.abs(c).max(axis=1) == 127).all()              # the largest element maps to +-127
+    err = np.abs(O.dequantize_rows(c, s) - rows)
+    assert (err <= s[:, None] * (0.5 + 1e-5)).all()          # half a step at most
+    # int8 halves the bf16 bytes of a cached row (the scale adds 4 bytes a row)
+    assert c[0].nbytes + 4 == 512 + 4 and c[0].nbytes * 2 == 512 * 2
+
+
 def test_global_cache_holds_one_unrotated_normalised_tensor():
     lay = layer(hq=8, hkv=1, d=16, kv_shared=True, theta=1e6, p=0.25)
     k = RNG.normal(size=(1, 5, 1, 16))
