@@ -73,6 +73,7 @@ def parse():
     ap.add_argument("--no-local", action="store_true", help="skip the local-layer prefill leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 6-layer stack decode leg")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode leg")
+    ap.add_argument("--no-int8", action="store_true", help="skip the int8-cache decode leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -296,6 +297,67 @@ def bench_multi_decode(args, torch, api, W, q_len=2):
     }
 
 
+def bench_int8_decode(args, torch, api, W):
+    """The global decode workload on an int8 K=V cache (codes + one fp32 scale per row)."""
+    from dataclasses import replace
+    wl = W.CONFIGS["global_decode"]
+    shape = wl.layer
+    dev = torch.device("cuda", 0)
+    lens = wl.lengths()
+    B, cap, D = wl.batch, wl.cache_cap(), shape.head_dim
+    lay = replace(api.Layer.from_shape(shape, torch.bfloat16), cache_format=1)
+    cache = api.new_cache(lay, B, cap, dev)
+    for b in range(B):
+        c, sc = W.int8_rows((1, shape.n_kv_heads, cap, D), 71 + b, dev)
+        cache.codes()[b:b + 1].copy_(c)
+        cache.scales()[b:b + 1].copy_(sc)
+        del c, sc
+    q = W.normal((B, shape.n_q_heads, D), wl.seed, "q_dec", torch.bfloat16, dev)
+    g_q = W.gains(D, wl.seed, "g_q", False, torch.bfloat16, dev)
+    seq = lens.to(dev)
+    maxlen = int(lens.max())
+    out = torch.empty_like(q)
+    ws = api.workspace(api.gemma_attn_decode_workspace_size(lay, B, maxlen), dev)
+
+    def step():
+        api.gemma_attn_decode(lay, q, g_q, cache, None, seq, maxlen, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    sec = timed(step, args.decode_steps, 0, torch)
+    api.profile_enable(False)
+    split_ms, n_split = api.profile_read("decode_splitk")
+    api.profile_reset()
+    kn = W.normal((B, shape.n_kv_heads, D), wl.seed, "k_new", torch.bfloat16, dev)
+    g_k = W.gains(D, wl.seed, "g_k", False, torch.bfloat16, dev)
+    pos = (lens - 1).to(dev)
+    api.profile_enable(True)
+    for _ in range(args.decode_steps):
+        api.kv_append(lay, kn, None, g_k, pos, cache, None)
+    torch.cuda.synchronize()
+    api.profile_enable(False)
+    append_ms, n_append = api.profile_read("kv_append")
+    api.profile_reset()
+    rows = int(lens.sum()) * shape.n_kv_heads
+    nbytes = rows * (D + 4)          # each cached row's codes and scale, once
+    del cache
+    torch.cuda.empty_cache()
+    split_ms /= max(n_split, 1)
+    return {
+        "workload": "global K=V layer decode on an int8 cache (codes + fp32 row scale): B=16, "
+                    "context ~ U[4096,131072] (seed 0), 32q/4kv, d=512",
+        "value": round(nbytes / sec / 1e9, 1), "unit": "GB/s", "ms_per_step": round(sec * 1e3, 4),
+        "tokens_per_s": round(B / sec, 1), "kv_bytes": nbytes,
+        "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V,int8>", "bound": "hbm",
+                     "achieved": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4), "avg_ms": round(split_ms, 4)},
+        "kv_append_avg_ms": round(append_ms / max(n_append, 1), 4),
+    }
+
+
 def bench_stack_decode(args, torch, api, W):
     """One decode step of a 6-layer stack (5 local + 1 global), each layer kv_append then decode."""
     wl_l, wl_g = W.CONFIGS["stack_decode_local"], W.CONFIGS["stack_decode_global"]
@@ -439,6 +501,11 @@ def main():
         }
     if not args.no_multi:
         line["multi_token_decode"] = bench_multi_decode(args, torch, api, W)
+    if not args.no_int8:
+        line["int8_decode"] = bench_int8_decode(args, torch, api, W)
+        if "decode" in line:
+            line["int8_decode"]["speedup_vs_bf16_cache"] = round(
+                line["decode"]["ms_per_step"] / line["int8_decode"]["ms_per_step"], 3)
     if not args.no_chunk:
         line["prefill_chunk"] = bench_prefill_chunk(args, torch, api, W)
     if not args.no_local:

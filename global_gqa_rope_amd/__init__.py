@@ -7,11 +7,14 @@ seeded synthetic inputs.
 
 from .api import (  # noqa: F401
     GemmaAttnError,
+    Int8Cache,
     Layer,
+    cache_bytes,
     gemma_attn_decode,
     gemma_attn_decode_workspace_size,
     gemma_attn_prefill,
     gemma_attn_prefill_workspace_size,
     kv_append,
+    new_cache,
     workspace,
 )

@@ -8,6 +8,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemma_attn.so")
 
 GA_BF16, GA_F32 = 0, 1
+GA_CACHE_NATIVE, GA_CACHE_INT8 = 0, 1
 STATUS = {0: "GA_OK", 1: "GA_EINVAL", 2: "GA_EUNSUPPORTED", 3: "GA_EWORKSPACE", 4: "GA_EHIP"}
 
 
@@ -23,6 +24,7 @@ class GaLayer(ctypes.Structure):
         ("norm_eps", ctypes.c_float),
         ("softmax_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("cache_format", ctypes.c_int32),
     ]
 
 
@@ -47,6 +49,7 @@ SIGNATURES = {
     "gemma_attn_decode": (_I, [_LP, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "gemma_attn_decode_multi_workspace_size": (_Z, [_LP, _I, _I, _I]),
     "gemma_attn_decode_multi": (_I, [_LP, _I, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
+    "gemma_attn_cache_bytes": (_Z, [_LP, _I, _I]),
     "gemma_attn_last_error": (ctypes.c_char_p, []),
     "gemma_attn_version": (ctypes.c_char_p, []),
     "gemma_attn_profile_enable": (None, [ctypes.c_int]),

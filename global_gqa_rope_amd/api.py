@@ -34,11 +34,12 @@ class Layer:
     norm_eps: float = 1e-6
     softmax_scale: float = 0.0     # <= 0: 1/sqrt(head_dim)
     dtype: torch.dtype = torch.bfloat16
+    cache_format: int = 0          # GA_CACHE_NATIVE; 1 = GA_CACHE_INT8 (global K=V layers, bf16)
 
     def struct(self) -> GaLayer:
         return GaLayer(self.n_q_heads, self.n_kv_heads, self.head_dim, self.window,
                        int(self.kv_shared), self.rope_theta, self.rope_fraction, self.norm_eps,
-                       self.softmax_scale, _DTYPES[self.dtype])
+                       self.softmax_scale, _DTYPES[self.dtype], int(self.cache_format))
 
     @property
     def group(self) -> int:
@@ -71,6 +72,61 @@ def _ptr(t: torch.Tensor | None, name: str, layer: Layer | None = None, shape=No
     return t.data_ptr()
 
 
+@dataclass(frozen=True)
+class Int8Cache:
+    """A GA_CACHE_INT8 cache: one uint8 buffer of gemma_attn_cache_bytes bytes
+    holding the int8 codes and then the per-row fp32 scales."""
+
+    buf: torch.Tensor
+    batch: int
+    cap: int
+    n_kv_heads: int
+    head_dim: int
+
+    def codes(self) -> torch.Tensor:
+        """Codes [B, Hkv, cap, d] (an int8 view)."""
+        n = self.batch * self.n_kv_heads * self.cap * self.head_dim
+        return self.buf[:n].view(torch.int8).view(self.batch, self.n_kv_heads, self.cap, self.head_dim)
+
+    def scales(self) -> torch.Tensor:
+        """Row scales [B, Hkv, cap] (a view)."""
+        n = self.batch * self.n_kv_heads * self.cap * self.head_dim
+        off = (n + 255) // 256 * 256
+        rows = self.batch * self.n_kv_heads * self.cap
+        return self.buf[off:off + 4 * rows].view(torch.float32).view(self.batch, self.n_kv_heads, self.cap)
+
+
+def cache_bytes(layer: Layer, batch: int, cap: int) -> int:
+    n = int(_lib.load().gemma_attn_cache_bytes(ctypes.byref(layer.struct()), batch, cap))
+    if n == 0 and batch > 0 and cap > 0:
+        raise GemmaAttnError(2, _lib.load().gemma_attn_last_error().decode(errors="replace"))
+    return n
+
+
+def new_cache(layer: Layer, batch: int, cap: int, device):
+    """A zeroed cache for this layer: a [B, Hkv, cap, d] tensor, or an Int8Cache."""
+    if layer.cache_format == _lib.GA_CACHE_INT8:
+        buf = torch.zeros(cache_bytes(layer, batch, cap), dtype=torch.uint8, device=device)
+        return Int8Cache(buf, batch, cap, layer.n_kv_heads, layer.head_dim)
+    return torch.zeros(batch, layer.n_kv_heads, cap, layer.head_dim, dtype=layer.dtype, device=device)
+
+
+def _cache(layer: Layer, cache, name: str, batch: int) -> tuple[int | None, int]:
+    """(pointer, cache_cap) of a cache argument (None: (None, 0))."""
+    if cache is None:
+        return None, 0
+    if layer.cache_format == _lib.GA_CACHE_INT8:
+        if not isinstance(cache, Int8Cache):
+            raise ValueError(f"{name}: an int8-cache layer takes an Int8Cache")
+        if cache.batch != batch or cache.n_kv_heads != layer.n_kv_heads or cache.head_dim != layer.head_dim:
+            raise ValueError(f"{name}: Int8Cache made for another batch or layer")
+        if cache.buf.numel() < cache_bytes(layer, batch, cache.cap):
+            raise ValueError(f"{name}: Int8Cache buffer too small")
+        return _ptr(cache.buf, name, dtype=torch.uint8), cache.cap
+    cap = cache.shape[2]
+    return _ptr(cache, name, layer, (batch, layer.n_kv_heads, cap, layer.head_dim)), cap
+
+
 def _stream(stream) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -98,16 +154,15 @@ def gemma_attn_prefill(layer: Layer, q, k, v, q_gain, k_gain, k_cache=None, v_ca
     need = gemma_attn_prefill_workspace_size(layer, B, S)
     if ws is None:
         ws = workspace(need, q.device)
-    cap = 0 if k_cache is None else k_cache.shape[2]
-    if k_cache is not None:
-        _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d))
-    if v_cache is not None:
-        _ptr(v_cache, "v_cache", layer, (B, Hkv, cap, d))
+    kc, cap = _cache(layer, k_cache, "k_cache", B)
+    vc, vcap = _cache(layer, v_cache, "v_cache", B)
+    if v_cache is not None and vcap != cap:
+        raise ValueError("k_cache and v_cache differ in capacity")
     st = _lib.load().gemma_attn_prefill(
         ctypes.byref(layer.struct()), B, S,
         _ptr(q, "q", layer, (B, S, Hq, d)), _ptr(k, "k", layer, (B, S, Hkv, d)),
         _ptr(v, "v", layer, (B, S, Hkv, d)), _ptr(q_gain, "q_gain", layer, (d,)),
-        _ptr(k_gain, "k_gain", layer, (d,)), _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+        _ptr(k_gain, "k_gain", layer, (d,)), kc, vc,
         cap, _ptr(out, "out", layer, (B, S, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8),
         ws.numel(), _stream(stream))
     _lib.check(st)
@@ -124,7 +179,7 @@ def gemma_attn_prefill_chunk(layer: Layer, start: int, q, k, q_gain, k_gain, k_c
     """Positions start .. start + chunk - 1 against k_cache slots 0 .. start - 1 (global K=V layers)."""
     B, T, Hq, d = q.shape
     Hkv = layer.n_kv_heads
-    cap = k_cache.shape[2]
+    kc, cap = _cache(layer, k_cache, "k_cache", B)
     if out is None:
         out = torch.empty_like(q)
     if ws is None:
@@ -132,7 +187,7 @@ def gemma_attn_prefill_chunk(layer: Layer, start: int, q, k, q_gain, k_gain, k_c
     st = _lib.load().gemma_attn_prefill_chunk(
         ctypes.byref(layer.struct()), B, int(start), T, _ptr(q, "q", layer, (B, T, Hq, d)),
         _ptr(k, "k", layer, (B, T, Hkv, d)), _ptr(q_gain, "q_gain", layer, (d,)),
-        _ptr(k_gain, "k_gain", layer, (d,)), _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d)), cap,
+        _ptr(k_gain, "k_gain", layer, (d,)), kc, cap,
         _ptr(out, "out", layer, (B, T, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8), ws.numel(),
         _stream(stream))
     _lib.check(st)
@@ -142,29 +197,28 @@ def gemma_attn_prefill_chunk(layer: Layer, start: int, q, k, q_gain, k_gain, k_c
 def kv_append(layer: Layer, k_new, v_new, k_gain, positions, k_cache, v_cache=None,
               stream=None) -> None:
     B, Hkv, d = k_new.shape
-    cap = k_cache.shape[2]
+    kc, cap = _cache(layer, k_cache, "k_cache", B)
+    vc, _ = _cache(layer, v_cache, "v_cache", B)
     st = _lib.load().kv_append(
         ctypes.byref(layer.struct()), B, _ptr(k_new, "k_new", layer, (B, Hkv, d)),
         _ptr(v_new, "v_new", layer, (B, Hkv, d)), _ptr(k_gain, "k_gain", layer, (d,)),
         _ptr(positions, "positions", dtype=torch.int32, shape=(B,)),
-        _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d)),
-        _ptr(v_cache, "v_cache", layer, (B, Hkv, cap, d)), cap, _stream(stream))
+        kc, vc, cap, _stream(stream))
     _lib.check(st)
 
 
 def gemma_attn_decode(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens, max_seq_len: int,
                       out=None, ws=None, stream=None) -> torch.Tensor:
     B, Hq, d = q.shape
-    Hkv = layer.n_kv_heads
-    cap = k_cache.shape[2]
+    kc, cap = _cache(layer, k_cache, "k_cache", B)
+    vc, _ = _cache(layer, v_cache, "v_cache", B)
     if out is None:
         out = torch.empty_like(q)
     if ws is None:
         ws = workspace(gemma_attn_decode_workspace_size(layer, B, max_seq_len), q.device)
     st = _lib.load().gemma_attn_decode(
         ctypes.byref(layer.struct()), B, _ptr(q, "q", layer, (B, Hq, d)),
-        _ptr(q_gain, "q_gain", layer, (d,)), _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d)),
-        _ptr(v_cache, "v_cache", layer, (B, Hkv, cap, d)), cap,
+        _ptr(q_gain, "q_gain", layer, (d,)), kc, vc, cap,
         _ptr(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,)), int(max_seq_len),
         _ptr(out, "out", layer, (B, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8), ws.numel(),
         _stream(stream))
@@ -181,16 +235,15 @@ def gemma_attn_decode_multi(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens,
                             out=None, ws=None, stream=None) -> torch.Tensor:
     """q [B, q_len, Hq, d]: the last q_len positions of each sequence against its cache."""
     B, T, Hq, d = q.shape
-    Hkv = layer.n_kv_heads
-    cap = k_cache.shape[2]
+    kc, cap = _cache(layer, k_cache, "k_cache", B)
+    vc, _ = _cache(layer, v_cache, "v_cache", B)
     if out is None:
         out = torch.empty_like(q)
     if ws is None:
         ws = workspace(gemma_attn_decode_multi_workspace_size(layer, B, T, max_seq_len), q.device)
     st = _lib.load().gemma_attn_decode_multi(
         ctypes.byref(layer.struct()), B, T, _ptr(q, "q", layer, (B, T, Hq, d)),
-        _ptr(q_gain, "q_gain", layer, (d,)), _ptr(k_cache, "k_cache", layer, (B, Hkv, cap, d)),
-        _ptr(v_cache, "v_cache", layer, (B, Hkv, cap, d)), cap,
+        _ptr(q_gain, "q_gain", layer, (d,)), kc, vc, cap,
         _ptr(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,)), int(max_seq_len),
         _ptr(out, "out", layer, (B, T, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8), ws.numel(),
         _stream(stream))

@@ -69,6 +69,7 @@ struct Derived {
   int group;
   int n_rot;
   int elem;
+  bool q8;                 // int8 K=V cache
   float scale;
   double log2_theta;
 };
@@ -93,6 +94,8 @@ ga_status check_layer(const ga_layer* L, Derived* out) {
   if (!(L->norm_eps > 0.f)) return fail(GA_EINVAL, "norm_eps must be > 0");
   if (!std::isfinite(L->softmax_scale)) return fail(GA_EINVAL, "softmax_scale must be finite");
   if (L->dtype != GA_BF16 && L->dtype != GA_F32) return fail(GA_EINVAL, "dtype must be GA_BF16 or GA_F32");
+  if (L->cache_format != GA_CACHE_NATIVE && L->cache_format != GA_CACHE_INT8)
+    return fail(GA_EINVAL, "cache_format must be GA_CACHE_NATIVE or GA_CACHE_INT8");
 
   const int G = L->n_q_heads / L->n_kv_heads;
   const int n_rot = static_cast<int>(rounded);
@@ -104,10 +107,15 @@ ga_status check_layer(const ga_layer* L, Derived* out) {
     return fail(GA_EUNSUPPORTED, "K=V layers are supported with window 0 only");
   if (L->kv_shared && n_rot != 64)
     return fail(GA_EUNSUPPORTED, "K=V layers rotate exactly 64 pairs on the fly (got %d)", n_rot);
+  if (L->cache_format == GA_CACHE_INT8 &&
+      (!L->kv_shared || L->dtype != GA_BF16 || L->head_dim != 512 || (G != 4 && G != 8)))
+    return fail(GA_EUNSUPPORTED, "the int8 cache is built for bf16 K=V layers with head_dim 512 and 4 or 8 "
+                                 "query heads per KV head");
   if (out) {
     out->group = G;
     out->n_rot = n_rot;
     out->elem = L->dtype == GA_BF16 ? 2 : 4;
+    out->q8 = L->cache_format == GA_CACHE_INT8;
     out->scale = L->softmax_scale > 0.f ? L->softmax_scale : 1.0f / std::sqrt(static_cast<float>(L->head_dim));
     out->log2_theta = std::log2(static_cast<double>(L->rope_theta));
   }
@@ -135,6 +143,20 @@ ga_status check_caches(const ga_layer* L, const void* k_cache, const void* v_cac
     return fail(GA_EINVAL, "cache_cap (%d) is smaller than the sequence (%d)", cache_cap, min_cap);
   }
   return GA_OK;
+}
+
+// int8 cache: codes [B][Hkv][cap][d] bytes, then the fp32 scales [B][Hkv][cap].
+size_t q8_scale_offset(const ga_layer* L, int batch, int cap) {
+  return align_up(static_cast<size_t>(batch) * L->n_kv_heads * cap * L->head_dim);
+}
+size_t cache_bytes(const ga_layer* L, const Derived& dv, int batch, int cap) {
+  const size_t rows = static_cast<size_t>(batch) * L->n_kv_heads * cap;
+  if (dv.q8) return q8_scale_offset(L, batch, cap) + rows * 4;
+  return rows * L->head_dim * dv.elem;
+}
+float* q8_scales(const ga_layer* L, const Derived& dv, void* cache, int batch, int cap) {
+  if (!dv.q8 || !cache) return nullptr;
+  return reinterpret_cast<float*>(static_cast<char*>(cache) + q8_scale_offset(L, batch, cap));
 }
 
 struct PrefillLayout {
@@ -252,6 +274,12 @@ const char* gemma_attn_last_error(void) { return g_error.c_str(); }
 
 const char* gemma_attn_version(void) { return "gemma_attn 0.1 (gfx950)"; }
 
+size_t gemma_attn_cache_bytes(const ga_layer* layer, int32_t batch, int32_t cache_cap) {
+  Derived dv;
+  if (check_layer(layer, &dv) != GA_OK || batch < 0 || cache_cap < 0) return 0;
+  return cache_bytes(layer, dv, batch, cache_cap);
+}
+
 size_t gemma_attn_prefill_workspace_size(const ga_layer* layer, int32_t batch, int32_t seq_len) {
   Derived dv;
   if (check_layer(layer, &dv) != GA_OK || batch < 0 || seq_len < 0) return 0;
@@ -319,6 +347,7 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
       pa.seq_len = seq_len; pa.seq_pad = lay.seq_pad; pa.n_kv_heads = layer->n_kv_heads; pa.n_rot = dv.n_rot;
       pa.window = layer->window; pa.kv_shared = layer->kv_shared; pa.cache_cap = cache_cap; pa.eps = layer->norm_eps;
       pa.pos0 = start;
+      pa.k_scales = q8_scales(layer, dv, k_cache, batch, cache_cap);
       st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "prefill prep launch");
     }
   }
@@ -372,11 +401,14 @@ ga_status kv_append(const ga_layer* layer, int32_t batch, const void* k_new, con
   if (!layer->kv_shared && !v_new) return fail(GA_EINVAL, "layer with a separate V needs v_new");
   st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
   if (st != GA_OK) return st;
+  if (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16)
+    return fail(GA_EINVAL, "the caches must be 16-byte aligned");
   ga::AppendArgs aa{};
   aa.k_new = k_new; aa.v_new = v_new; aa.k_gain = k_gain; aa.positions = positions;
   aa.k_cache = k_cache; aa.v_cache = v_cache; aa.n_kv_heads = layer->n_kv_heads; aa.n_rot = dv.n_rot;
   aa.window = layer->window; aa.kv_shared = layer->kv_shared; aa.cache_cap = cache_cap; aa.eps = layer->norm_eps;
   aa.log2_theta = dv.log2_theta;
+  aa.k_scales = q8_scales(layer, dv, k_cache, batch, cache_cap);
   ProfScope ps(static_cast<hipStream_t>(stream), 4);
   return hip_status(ga::launch_kv_append(aa, layer->dtype, layer->head_dim, batch, static_cast<hipStream_t>(stream)),
                     "kv_append launch");
@@ -410,8 +442,10 @@ ga_status gemma_attn_decode_multi(const ga_layer* layer, int32_t batch, int32_t 
     return fail(GA_EUNSUPPORTED, "fp32 decode with head_dim 512 and a separate V cache is not built");
   st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
   if (st != GA_OK) return st;
-  if (static_cast<int64_t>(cache_cap) * layer->head_dim * dv.elem > INT32_MAX)
+  if (static_cast<int64_t>(cache_cap) * layer->head_dim * (dv.q8 ? 1 : dv.elem) > INT32_MAX)
     return fail(GA_EUNSUPPORTED, "cache_cap %d: one head's cache must stay under 2 GiB for decode", cache_cap);
+  if (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16)
+    return fail(GA_EINVAL, "the caches must be 16-byte aligned");
   const size_t need = decode_bytes(layer, dv, batch, q_len, max_seq_len);
   st = check_workspace(workspace, workspace_bytes, need);
   if (st != GA_OK) return st;
@@ -430,6 +464,7 @@ ga_status gemma_attn_decode_multi(const ga_layer* layer, int32_t batch, int32_t 
   da.batch = batch; da.n_q_heads = layer->n_q_heads; da.n_kv_heads = layer->n_kv_heads; da.n_rot = dv.n_rot;
   da.window = layer->window; da.cache_cap = cache_cap; da.max_seq_len = max_seq_len; da.n_wgs = plan.n_wgs;
   da.q_len = q_len; da.slot_floats = static_cast<int>(plan.slot_floats);
+  da.k_scales = q8_scales(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
   da.eps = layer->norm_eps; da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
   return hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
                                       static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),

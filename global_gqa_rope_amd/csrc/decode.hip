@@ -35,23 +35,33 @@ namespace ga {
 
 constexpr int kLdsLimit = 160 * 1024;
 
-template <typename T, int D, int G, bool SHARED>
+// Q8: the K=V cache holds int8 rows (codes c and one fp32 scale s per row,
+// standing for c s).  Each tile's codes and scales are copied into a staging
+// buffer; the codes, exact in bf16, are expanded into the bf16 tile the native
+// cache is copied into, so the score and value products are the same code for
+// both formats, and the row scales are applied in fp32: to each score
+// (q . c s = (q . c) s) and to each softmax weight before it meets the codes
+// as values (p (c s) = (p s) c).
+template <typename T, int D, int G, bool SHARED, bool Q8 = false>
 struct DecodeCfg {
   static constexpr int KT = 16;                       // keys per wave tile
+  static constexpr int kD = D;
   static constexpr int kSz = int(sizeof(T));
   static constexpr int kRot = SHARED ? 64 : 0;        // pairs rotated on the fly
   static constexpr int kRotSteps = 2 * kRot / 32;     // QK^T steps that cover rotated dims
   static constexpr int kRowBytes = D * kSz;           // one key row
   static constexpr int kKBytes = KT * kRowBytes;      // key tile (the values too for K=V)
   static constexpr int kTileBytes = SHARED ? kKBytes : 2 * kKBytes;   // + value tile
-  static constexpr int kBufs = 2;                     // tiles in LDS per wave
+  static constexpr int kBufs = Q8 ? 1 : 2;            // tiles in LDS per wave
+  static constexpr int kCodeBytes = KT * D;           // Q8: one tile's codes
+  static constexpr int kStageBytes = Q8 ? kCodeBytes + 256 : 0;   // codes, then 64 scale slots
   static constexpr int kQSteps = D / 32;              // QK^T reduction steps
   static constexpr int kDBlocks = D / 16;             // PV output blocks of 16 dims
   static constexpr int kFragBytes = 64 * 8 * kSz;     // one query operand fragment
   static constexpr int kQBytes = kQSteps * kFragBytes;
   static constexpr int kFineBytes = 16 * kRot * 8;    // cos/sin(j w_i), j < 16, i < kRot
   static constexpr int kCoarseBytes = kRot * 8;       // per wave: cos/sin(key0 w_i)
-  static constexpr int kPerWaveBytes = kBufs * kTileBytes + kCoarseBytes;
+  static constexpr int kPerWaveBytes = kBufs * kTileBytes + 2 * kStageBytes + kCoarseBytes;
   static constexpr int kMiscBytes = 64;               // partition scratch
   static constexpr int kCommonBytes = kQBytes + kFineBytes + kMiscBytes;
   static constexpr int kWaves = (4 * kPerWaveBytes + kCommonBytes <= kLdsLimit)   ? 4
@@ -59,8 +69,10 @@ struct DecodeCfg {
                                                                                   : 1;
   static constexpr int kDmaPerTile = kTileBytes / 1024;
   static constexpr int kKDma = kKBytes / 1024;
-  // LDS map: [wave][buf] tiles | [wave] coarse angles | query operand | fine angles | misc
-  static constexpr int kCoarseOff = kWaves * kBufs * kTileBytes;
+  // LDS map: [wave][buf] tiles | [wave][2] staging (Q8) | [wave] coarse angles |
+  // query operand | fine angles | misc
+  static constexpr int kStageOff = kWaves * kBufs * kTileBytes;
+  static constexpr int kCoarseOff = kStageOff + kWaves * 2 * kStageBytes;
   static constexpr int kQOff = kCoarseOff + kWaves * kCoarseBytes;
   static constexpr int kFineOff = kQOff + kQBytes;
   static constexpr int kMiscOff = kFineOff + kFineBytes;
@@ -68,6 +80,7 @@ struct DecodeCfg {
   static_assert(kLdsBytes <= kLdsLimit, "LDS budget");
   static_assert(kRowBytes / 16 >= 16, "row swizzle needs 16 chunks per row");
   static_assert(kTileBytes % 1024 == 0 && kDmaPerTile < 64, "tile copy");
+  static_assert(!Q8 || (SHARED && sizeof(T) == 2 && kCodeBytes % 1024 == 0), "int8 tiles: bf16 K=V");
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -138,6 +151,48 @@ __device__ __forceinline__ void issue_tile(lds_char* dst, BufRsrc rk, BufRsrc rv
       const int key = min(key0 + r, nkeys - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, slot, 16, key * C::kRowBytes + (row_chunk(r, s) << 4), 0, 0, 0);
     }
+  }
+}
+
+// Q8: copy one tile's codes (16 rows of D bytes, natural order) and the 16
+// row scales into a staging buffer.  Lane l of the scale copy fetches the
+// scale of row l (clamped to the sequence); slots 16..63 are not read.
+template <typename C>
+__device__ __forceinline__ void issue_q8(lds_char* dst, BufRsrc rc, BufRsrc rs, int key0, int nkeys, int lane) {
+  constexpr int kRowsPerPiece = 1024 / C::kD;     // D-byte code rows per 1 KiB
+  constexpr int kChunksPerRow = C::kD / 16;
+#pragma unroll
+  for (int i = 0; i < C::kCodeBytes / 1024; ++i) {
+    const int r = i * kRowsPerPiece + lane / kChunksPerRow;
+    const int key = min(key0 + r, nkeys - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, dst + i * 1024, 16, key * C::kD + (lane % kChunksPerRow) * 16,
+                                             0, 0, 0);
+  }
+  const int key = min(key0 + lane, nkeys - 1);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + C::kCodeBytes, 4, key * 4, 0, 0, 0);
+}
+
+// Q8: expand the staged codes into the bf16 tile (|c| <= 127: exact in bf16).
+// Lane l writes the 16-byte chunk l of every row at the row swizzle.
+template <typename C>
+__device__ __forceinline__ void expand_q8(const lds_char* __restrict__ stage, lds_char* __restrict__ tile, int lane) {
+  constexpr int kD = C::kD;
+  static_assert(kD == 64 * 8, "one 8-code piece per lane and row");
+#pragma unroll
+  for (int r = 0; r < C::KT; ++r) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(stage + r * kD + 8 * lane);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 packed;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {   // sign-extend and convert each byte, pack pairs
+      const f32x2 x{static_cast<float>(static_cast<int8_t>(w[j / 4] >> (8 * (j % 4)))),
+                    static_cast<float>(static_cast<int8_t>(w[j / 4] >> (8 * (j % 4 + 1))))};
+      packed[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+    }
+    const bf16x8 v = __builtin_bit_cast(bf16x8, packed);
+    *(__attribute__((address_space(3))) bf16x8*)(tile + r * C::kRowBytes + (row_chunk(r, lane) << 4)) = v;
   }
 }
 
@@ -305,9 +360,9 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
   return x;
 }
 
-template <typename T, int D, int G, bool SHARED>
-__global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void decode_kernel(DecodeArgs a) {
-  using C = DecodeCfg<T, D, G, SHARED>;
+template <typename T, int D, int G, bool SHARED, bool Q8>
+__global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) void decode_kernel(DecodeArgs a) {
+  using C = DecodeCfg<T, D, G, SHARED, Q8>;
   static_assert(C::KT == kDecodeTile, "tile size");
   const int kSlot = a.slot_floats;
   const int ncol = G * a.q_len;   // query columns: column c is token c / G, head c % G (<= 16)
@@ -372,7 +427,9 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
   const uint32_t smem0 = lds_addr(smem);
   const uint32_t tiles = smem0 + wave * C::kBufs * C::kTileBytes;
   lds_char* const tile_buf = (lds_char*)smem + wave * C::kBufs * C::kTileBytes;
-  const uint32_t span = static_cast<uint32_t>(a.cache_cap) * C::kRowBytes;   // < 2^31 (checked on the host)
+  lds_char* const stage_buf = (lds_char*)smem + C::kStageOff + wave * 2 * C::kStageBytes;   // Q8
+  // bytes of one head's cache rows: < 2^31 (checked on the host)
+  const uint32_t span = static_cast<uint32_t>(a.cache_cap) * (Q8 ? C::kD : C::kRowBytes);
   Seg pf = cur;
   auto issue = [&](lds_char* dst, int k) {
     const int g = t_begin + wave + C::kWaves * k;
@@ -380,10 +437,15 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
     while (g >= pf.T + pf.n) seg_next(pf, a);
     const int64_t head = static_cast<int64_t>(pf.b) * a.n_kv_heads + pf.kvh;
     const BufRsrc rk = make_rsrc(static_cast<const char*>(a.k_cache) + head * span, span);
-    const BufRsrc rv = SHARED ? rk : make_rsrc(static_cast<const char*>(a.v_cache) + head * span, span);
-    issue_tile<C>(dst, rk, rv, (g - pf.T) * C::KT, pf.keys, lane);
+    if constexpr (Q8) {
+      const BufRsrc rs = make_rsrc(a.k_scales + head * a.cache_cap, static_cast<uint32_t>(a.cache_cap) * 4);
+      issue_q8<C>(dst, rk, rs, (g - pf.T) * C::KT, pf.keys, lane);
+    } else {
+      const BufRsrc rv = SHARED ? rk : make_rsrc(static_cast<const char*>(a.v_cache) + head * span, span);
+      issue_tile<C>(dst, rk, rv, (g - pf.T) * C::KT, pf.keys, lane);
+    }
   };
-  issue(tile_buf, 0);
+  issue(Q8 ? stage_buf : tile_buf, 0);
 
   // ---- rotation rates of the lane's pairs lane + 64 m (fp64, one exp2 each) ------
   constexpr int kPairsPerLane = D / 128;
@@ -506,13 +568,19 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
       const int g = t_begin + wave + C::kWaves * k;
       if (g >= p_end) break;
       const int key0 = (g - cur.T) * C::KT;
-      const uint32_t buf = (k & 1) * C::kTileBytes;
+      const uint32_t buf = Q8 ? 0u : (k & 1) * C::kTileBytes;
       wait_vm_le<0>();   // tile k has landed: it is the wave's only copy in flight
-      // The step runs in a function whose two buffers are restrict pointers:
-      // the compiler then knows the copy of tile k + 1 into `nxt` does not
-      // feed the reads of `cur_buf`, and adds no wait for it before them.
-      auto step = [&](const lds_char* __restrict__ cur_buf, lds_char* __restrict__ nxt) {
+      // The step runs in a function whose buffers are restrict pointers: the
+      // compiler then knows the copy of tile k + 1 into `nxt` does not feed
+      // the reads of `cur_buf` (or of `stage`), and adds no wait for it before
+      // them.
+      auto step = [&](lds_char* __restrict__ cur_buf, lds_char* __restrict__ nxt,
+                      const lds_char* __restrict__ stage) {
         issue(nxt, k + 1);
+        if constexpr (Q8) {
+          expand_q8<C>(stage, cur_buf, lane);
+          asm volatile("" ::: "memory");   // the tile's writes come before its operand reads
+        }
 
         // S^T = K~ Q~^T; the lane's A operand is key row hcol, dims 32u + 8kg .. +7.
         // Reads run kQAhead steps ahead of the MFMAs.
@@ -530,6 +598,11 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
           __builtin_amdgcn_sched_barrier(0);
         }
         f32x4 s = sa + sb;
+        f32x4 row_scale;   // Q8: scales of the lane's keys 4 kg .. 4 kg + 3
+        if constexpr (Q8) {
+          row_scale = *(const __attribute__((address_space(3))) f32x4*)(stage + C::kCodeBytes + 16 * kg);
+          s *= row_scale;
+        }
         if constexpr (SHARED) {   // publish the wave's next tile's coarse angles
           const f32x2 c = coarse_l;
           coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
@@ -556,7 +629,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
         for (int v = 0; v < 4; ++v) {
           const float p = __builtin_amdgcn_exp2f(s[v] - m_use);
           psum += p;
-          frag_set(pf4, v, p);
+          frag_set(pf4, v, Q8 ? p * row_scale[v] : p);
         }
         if (rescale) {
   #pragma unroll
@@ -578,7 +651,11 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED>::kWaves * 64), 1) void 
         }
         lds_fence();   // this tile's LDS reads are done before its buffer is refilled
       };
-      step(tile_buf + buf, tile_buf + (buf ^ C::kTileBytes));
+      if constexpr (Q8) {
+        step(tile_buf, stage_buf + ((k + 1) & 1) * C::kStageBytes, stage_buf + (k & 1) * C::kStageBytes);
+      } else {
+        step(tile_buf + buf, tile_buf + (buf ^ C::kTileBytes), nullptr);
+      }
     }
 
     // ---- this wave's partial result for the segment --------------------------------
@@ -672,11 +749,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-template <typename T, int D, int G, bool SHARED>
+template <typename T, int D, int G, bool SHARED, bool Q8 = false>
 static hipError_t launch_one(const DecodeArgs& a, hipStream_t s, LaunchTimer timer) {
-  using C = DecodeCfg<T, D, G, SHARED>;
+  using C = DecodeCfg<T, D, G, SHARED, Q8>;
   if (timer) timer(s, 2, true);
-  hipLaunchKernelGGL((decode_kernel<T, D, G, SHARED>), dim3(a.n_wgs), dim3(C::kWaves * 64), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, SHARED, Q8>), dim3(a.n_wgs), dim3(C::kWaves * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (timer) timer(s, 2, false);
   if (e != hipSuccess) return e;
@@ -690,6 +767,18 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t s, LaunchTimer tim
 
 template <typename T, int D, bool SHARED>
 static hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t s, LaunchTimer tm) {
+  if constexpr (SHARED && D == 512 && sizeof(T) == 2) {
+    static_assert(DecodeCfg<T, D, 8, SHARED, true>::kWaves == DecodeCfg<T, D, 8, SHARED>::kWaves,
+                  "the plan and the merge assume one wave count for both cache formats");
+    if (a.k_scales) {   // int8 K=V cache
+      switch (group) {
+        case 8: return launch_one<T, D, 8, SHARED, true>(a, s, tm);
+        case 4: return launch_one<T, D, 4, SHARED, true>(a, s, tm);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
+  if (a.k_scales) return hipErrorInvalidValue;
   switch (group) {
     case 1: return launch_one<T, D, 1, SHARED>(a, s, tm);
     case 2: return launch_one<T, D, 2, SHARED>(a, s, tm);

@@ -17,6 +17,24 @@ __global__ void rope_table_kernel(f32x2* __restrict__ table, int n_pos, int n_ro
   }
 }
 
+// int8 K=V cache rows: codes round-half-even(x / s), s = max |x| / 127, kept
+// as two's-complement bytes.  The division is the correctly rounded float32
+// one, so equal inputs give equal codes.
+__device__ __forceinline__ uint2 q8_pack8(const float (&x)[8], float s) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float c = s > 0.f ? fminf(fmaxf(rintf(x[j] / s), -127.f), 127.f) : 0.f;
+    w[j / 4] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xffu) << (8 * (j % 4));
+  }
+  return uint2{w[0], w[1]};
+}
+__device__ __forceinline__ void q8_unpack8(float (&x)[8], uint2 u, float s) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    x[j] = static_cast<float>(static_cast<int8_t>((j < 4 ? u.x : u.y) >> (8 * (j % 4)))) * s;
+}
+
 // One workgroup per (tile of kPrepTile key positions, kv head, batch).
 // Thread t owns key row r = t / 8 of the tile and the 8-element chunks
 // i * 8 + t % 8 of that row, so eight neighbouring lanes cover 64 contiguous
@@ -51,13 +69,19 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   vec8 kin[kMine], vin[kMine], gin[kMine];
   f32x2 cs[kMine][4];
   const T* __restrict__ cache_row = static_cast<const T*>(a.k_cache) + (head_base * a.cache_cap + pos) * D;
+  const bool q8 = a.k_scales != nullptr;                  // int8 K=V cache
+  const uint8_t* __restrict__ code_row = static_cast<const uint8_t*>(a.k_cache) + (head_base * a.cache_cap + pos) * D;
+  uint2 qin[kMine];
+  float q_scale = 0.f;
 #pragma unroll
   for (int i = 0; i < kMine; ++i) {
     const int d0 = (i * 8 + c8) * 8;
-    kin[i] = *reinterpret_cast<const vec8*>((cached ? cache_row : k + src_row) + d0);
+    if (cached && q8) qin[i] = *reinterpret_cast<const uint2*>(code_row + d0);
+    else kin[i] = *reinterpret_cast<const vec8*>((cached ? cache_row : k + src_row) + d0);
     gin[i] = *reinterpret_cast<const vec8*>(gk + d0);
     if (has_v) vin[i] = *reinterpret_cast<const vec8*>(v + src_row + d0);
   }
+  if (cached && q8) q_scale = a.k_scales[head_base * a.cache_cap + pos];
   // (cos, sin) of the chunk's four pairs; pairs >= n_rot read a clamped entry
   // of the same row and are not used
   if (a.n_rot > 0) {
@@ -72,12 +96,16 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   float x[kMine][8];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMine; ++i)
+  for (int i = 0; i < kMine; ++i) {
+    if (cached && q8) {
+      q8_unpack8(x[i], qin[i], q_scale);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      x[i][j] = (valid || cached) ? to_f32(kin[i][j]) : 0.f;
-      ss += x[i][j] * x[i][j];
+      for (int j = 0; j < 8; ++j) x[i][j] = (valid || cached) ? to_f32(kin[i][j]) : 0.f;
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += x[i][j] * x[i][j];
+  }
   ss += wave_xor(ss, 1);
   ss += wave_xor(ss, 2);
   ss += wave_xor(ss, 4);
@@ -95,7 +123,23 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   T* __restrict__ wv = static_cast<T*>(a.ws_v) + row * D;
 
   // Value row.  K=V: the normalised, unrotated key, which is also what the
-  // cache keeps.  Otherwise the raw v (zeros past the sequence).
+  // cache keeps (int8 caches: its codes and the row's scale).  Otherwise the
+  // raw v (zeros past the sequence).
+  if (!has_v && q8 && kc && valid) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMine; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[i][j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+    const float sc = amax / 127.0f;
+    uint8_t* codes = static_cast<uint8_t*>(a.k_cache) + (head_base * a.cache_cap + pos) * D;
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) *reinterpret_cast<uint2*>(codes + (i * 8 + c8) * 8) = q8_pack8(x[i], sc);
+    if (c8 == 0) a.k_scales[head_base * a.cache_cap + pos] = sc;
+  }
   vec8 vout[kMine];
 #pragma unroll
   for (int i = 0; i < kMine; ++i) {
@@ -106,7 +150,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) vout[i][j] = from_f32<T>(x[i][j]);
-      if (kc && valid) *reinterpret_cast<vec8*>(kc + (head_base * a.cache_cap + pos) * D + d0) = vout[i];
+      if (kc && valid && !q8) *reinterpret_cast<vec8*>(kc + (head_base * a.cache_cap + pos) * D + d0) = vout[i];
     }
     *reinterpret_cast<vec8*>(wv + d0) = vout[i];
   }
@@ -180,6 +224,24 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
 #pragma unroll
   for (int j = 0; j < kPer; ++j) x[j] = x[j] * rstd * to_f32(gk[j]);
 
+  if (a.k_scales) {   // int8 K=V cache: codes and the row's scale
+    static_assert(kPer == 8 || kPer == 4, "8 or 4 elements per lane");
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) amax = fmaxf(amax, fabsf(x[j]));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+    const float sc = amax / 127.0f;
+    uint8_t* codes = static_cast<uint8_t*>(a.k_cache) + (head_base * a.cache_cap + slot) * D + l * kPer;
+    float x8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x8[j] = j < kPer ? x[j] : 0.f;
+    const uint2 u = q8_pack8(x8, sc);
+    if constexpr (kPer == 8) *reinterpret_cast<uint2*>(codes) = u;
+    else *reinterpret_cast<uint32_t*>(codes) = u.x;
+    if (l == 0) a.k_scales[head_base * a.cache_cap + slot] = sc;
+    return;
+  }
   T* __restrict__ kc = static_cast<T*>(a.k_cache) + (head_base * a.cache_cap + slot) * D + l * kPer;
   if (!a.kv_shared) {
 #pragma unroll

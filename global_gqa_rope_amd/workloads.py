@@ -29,7 +29,7 @@ from dataclasses import dataclass, replace
 import torch
 
 TAGS = {"q": 1, "k": 2, "v": 3, "g_q": 4, "g_k": 5, "lens": 6, "k_cache": 7,
-        "v_cache": 8, "k_new": 9, "v_new": 10, "q_dec": 11}
+        "v_cache": 8, "k_new": 9, "v_new": 10, "q_dec": 11, "q8_codes": 12, "q8_scales": 13}
 
 
 @dataclass(frozen=True)
@@ -78,6 +78,17 @@ def gains(d: int, seed: int, tag: str, unit: bool, dtype, device="cpu"):
     if unit:
         return torch.ones(d, dtype=dtype, device=device)
     return normal((d,), seed, tag, dtype, device, mean=1.0, std=0.1)
+
+
+def int8_rows(shape, seed: int, device="cpu") -> tuple[torch.Tensor, torch.Tensor]:
+    """A filled int8 K=V cache of rows shape[:-1] x shape[-1] codes: codes
+    uniform in [-127, 127] (int8), and one scale per row uniform in
+    [0.01, 0.03] (float32; rows of rms near 1 give scales of about 0.025)."""
+    codes = torch.randint(-127, 128, tuple(shape), generator=_gen(seed, "q8_codes", device), dtype=torch.int8,
+                          device=device)
+    scales = torch.rand(tuple(shape[:-1]), generator=_gen(seed, "q8_scales", device), dtype=torch.float32,
+                        device=device)
+    return codes, scales.mul_(0.02).add_(0.01)
 
 
 def uniform_lengths(n: int, lo: int, hi: int, seed: int) -> torch.Tensor:

@@ -80,7 +80,31 @@ typedef struct {
   float norm_eps;         /* QKNorm epsilon, > 0 (1e-6)                       */
   float softmax_scale;    /* <= 0 selects 1/sqrt(d)                           */
   int32_t dtype;          /* ga_dtype of every tensor; accumulation is fp32   */
+  int32_t cache_format;   /* ga_cache_format of k_cache (0: dtype elements)   */
 } ga_layer;
+
+/*
+ * Cache formats.  GA_CACHE_INT8 (global K=V layers with dtype GA_BF16,
+ * head_dim 512 and 4 or 8 query heads per KV head; others: GA_EUNSUPPORTED)
+ * keeps each cached row (one position of one KV head) as d int8 codes and one
+ * fp32 scale s = max_i |k_i| / 127, codes c_i = round-half-even(k_i / s), the
+ * row standing for c_i * s: the int8 KV cache of the pages' 32K memory table
+ * ("Gemma 4 技术报告：开源全模态密集 + MoE 模型家族，长上下文与端侧高效是本代核心",
+ * table "显存占用（32k 上下文，文本 only，int8 KV cache）"), which leaves the int8
+ * mapping open.  One k_cache buffer holds, for B sequences of cache_cap slots:
+ *   int8  [B][Hkv][cache_cap][d]   c_i (two's complement, -127 .. 127)
+ *   then, at byte offset round_up(B * Hkv * cache_cap * d, 256),
+ *   float [B][Hkv][cache_cap]      s
+ * Every call that takes k_cache and batch finds the scales there; a cache is
+ * filled and read with the same batch.  An all-zero row has s = 0 and codes 0.
+ * Prefill attends over the prompt's own keys at full precision and only
+ * writes the cache; decode and a later prefill chunk read cached rows back as
+ * c_i * s.  Decode streams about half the bytes of a bf16 cache.
+ */
+typedef enum { GA_CACHE_NATIVE = 0, GA_CACHE_INT8 = 1 } ga_cache_format;
+
+/* Bytes of one cache tensor (k_cache; v_cache alike) of this layer. */
+size_t gemma_attn_cache_bytes(const ga_layer* layer, int32_t batch, int32_t cache_cap);
 
 /* Bytes of scratch gemma_attn_prefill needs for this batch and length. */
 size_t gemma_attn_prefill_workspace_size(const ga_layer* layer, int32_t batch,

@@ -38,8 +38,8 @@ def test_version(lib):
     assert lib.gemma_attn_version().startswith(b"gemma_attn")
 
 
-def L(hq=32, hkv=4, d=512, window=0, shared=1, theta=1e6, p=0.25, eps=1e-6, dtype=0):
-    return _lib.GaLayer(hq, hkv, d, window, shared, theta, p, eps, 0.0, dtype)
+def L(hq=32, hkv=4, d=512, window=0, shared=1, theta=1e6, p=0.25, eps=1e-6, dtype=0, cache=0):
+    return _lib.GaLayer(hq, hkv, d, window, shared, theta, p, eps, 0.0, dtype, cache)
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
@@ -64,6 +64,10 @@ def prefill(lib, layer, B=1, S=16, v=None, k_cache=None, v_cache=None, cap=0, ws
     (L(hq=48, hkv=3), 2, "1, 2, 4, 8"),
     (L(window=64), 2, "window 0"),
     (L(p=0.5), 2, "64 pairs"),
+    (L(cache=2), 1, "cache_format"),
+    (L(cache=1, dtype=1), 2, "int8 cache"),
+    (L(cache=1, hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0), 2, "int8 cache"),
+    (L(cache=1, hq=8, hkv=4), 2, "int8 cache"),
 ])
 def test_layer_validation(lib, layer, status, msg):
     assert prefill(lib, layer) == status
@@ -169,3 +173,26 @@ def decode_ws(B, hkv, G, d, keys, waves=4):
     P = min(1024 // waves, -(-tiles // (2 * waves)))
     prefix = -(-(B + 1) * 4 // 256) * 256
     return prefix + waves * (P + B * hkv) * (G * d + 64) * 4
+
+
+def test_cache_bytes(lib):
+    g = L()
+    assert lib.gemma_attn_cache_bytes(ctypes.byref(g), 2, 100) == 2 * 4 * 100 * 512 * 2
+    q8 = L(cache=1)
+    # codes [B,Hkv,cap,d] bytes, padded to 256 B, then one fp32 scale per row
+    codes = 2 * 4 * 100 * 512
+    assert lib.gemma_attn_cache_bytes(ctypes.byref(q8), 2, 100) == -(-codes // 256) * 256 + 2 * 4 * 100 * 4
+    e = L(hq=8, hkv=2, cache=1)
+    codes = 3 * 2 * 7 * 512
+    assert lib.gemma_attn_cache_bytes(ctypes.byref(e), 3, 7) == -(-codes // 256) * 256 + 3 * 2 * 7 * 4
+    assert lib.gemma_attn_cache_bytes(ctypes.byref(L(cache=5)), 1, 1) == 0   # invalid layer
+
+
+def test_int8_cache_alignment_is_checked(lib):
+    q8 = L(cache=1)
+    odd = ctypes.c_void_p(0x1008)
+    st = lib.gemma_attn_decode(ctypes.byref(q8), 1, FAKE, FAKE, odd, None, 64, FAKE, 64, FAKE, FAKE, 1 << 40, None)
+    assert st == 1 and "16-byte" in lib.gemma_attn_last_error().decode()
+    pos = FAKE
+    st = lib.kv_append(ctypes.byref(q8), 1, FAKE, None, FAKE, pos, odd, None, 64, None)
+    assert st == 1 and "16-byte" in lib.gemma_attn_last_error().decode()
