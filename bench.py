@@ -36,12 +36,18 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 # still match; after any change to them the figure is stale and reads null.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "162d930e93df2ec2",
-                     "bytes": 23110933109},
-    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "162d930e93df2ec2",
-                           "bytes": 8591068586},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2e66e576819ab91a",
-                      "bytes": 4289395275},
+    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "f8b0a36566b67a46",
+                     "bytes": 16349689057},
+    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "f8b0a36566b67a46",
+                           "bytes": 8590227589},
+    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "f8b0a36566b67a46",
+                           "bytes": 4626512726},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d8286757eaa8047a",
+                      "bytes": 4288964062},
+    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d8286757eaa8047a",
+                            "bytes": 4312569210},
+    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d8286757eaa8047a",
+                           "bytes": 2173227349},
 }
 
 
@@ -249,7 +255,9 @@ def bench_prefill_chunk(args, torch, api, W, start=28672):
         "flops_per_step": flops, "prep_avg_ms": round(prep_ms / max(n_prep, 1), 4),
         "roofline": {"kernel": "prefill_attn_kernel<bf16,512,8>", "bound": "mfma", "achieved": round(attn, 2),
                      "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn / MI355X_BF16_DENSE_TFLOPS, 4), "avg_ms": round(attn_ms, 4)},
+                     "frac": round(attn / MI355X_BF16_DENSE_TFLOPS, 4),
+                     "traffic": measured_traffic("chunk_prefill_attn"),
+                     "avg_ms": round(attn_ms, 4)},
     }
 
 
@@ -293,7 +301,9 @@ def bench_multi_decode(args, torch, api, W, q_len=2):
         "tokens_per_s": round(B * q_len / sec, 1), "kv_bytes": nbytes,
         "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V>", "bound": "hbm",
                      "achieved": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
-                     "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4), "avg_ms": round(split_ms, 4)},
+                     "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4),
+                     "traffic": measured_traffic("multi_decode_splitk"),
+                     "avg_ms": round(split_ms, 4)},
     }
 
 
@@ -353,7 +363,9 @@ def bench_int8_decode(args, torch, api, W):
         "tokens_per_s": round(B / sec, 1), "kv_bytes": nbytes,
         "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V,int8>", "bound": "hbm",
                      "achieved": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
-                     "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4), "avg_ms": round(split_ms, 4)},
+                     "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4),
+                     "traffic": measured_traffic("int8_decode_splitk"),
+                     "avg_ms": round(split_ms, 4)},
         "kv_append_avg_ms": round(append_ms / max(n_append, 1), 4),
     }
 
