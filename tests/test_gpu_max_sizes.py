@@ -1,0 +1,66 @@
+"""GPU parity at the largest sizes the workloads reach: a 128K-position global
+prefill and decode steps against 256K-position caches (bf16 and int8), each
+checked on sampled rows the float64 oracle computes one by one."""
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from global_gqa_rope_amd import api
+from global_gqa_rope_amd import workloads as W
+from tests.gpu_helpers import api_layer, assert_close, device, oracle_layer, to64
+from tests.test_gpu_parity import _sampled_prefill
+
+pytestmark = pytest.mark.gpu
+
+CTX_256K = 262144
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_global_prefill_128k_sampled_rows():
+    wl = W.with_seq(W.CONFIGS["global_prefill_32k"], 131072)
+    _sampled_prefill(wl, [0, 1, 65535, 100000, 131071], [0], "global prefill 128K")
+
+
+def test_global_decode_256k_context():
+    shape, dev = W.GLOBAL_LAYER, device()
+    lens = torch.tensor([CTX_256K, 150001], dtype=torch.int32)
+    B, D = len(lens), shape.head_dim
+    kc = W.normal((B, shape.n_kv_heads, CTX_256K, D), 81, "k_cache", torch.bfloat16, dev)
+    q = W.normal((B, shape.n_q_heads, D), 81, "q_dec", torch.bfloat16, dev)
+    g_q = W.gains(D, 81, "g_q", False, torch.bfloat16, dev)
+    out = api.gemma_attn_decode(api_layer(shape, torch.bfloat16), q, g_q, kc, None, lens.to(dev), CTX_256K)
+    torch.cuda.synchronize()
+    ol = oracle_layer(shape)
+    for b in range(B):
+        L = int(lens[b])
+        ref = O.decode_from_cache(ol, to64(q[b:b + 1]), to64(g_q), to64(kc[b:b + 1, :, :L]), None, np.array([L]))
+        assert_close(out[b:b + 1], ref, torch.bfloat16, f"decode at {L} cached positions")
+
+
+def test_int8_decode_256k_context():
+    shape, dev = W.GLOBAL_LAYER, device()
+    D = shape.head_dim
+    lay = replace(api_layer(shape, torch.bfloat16), cache_format=1)
+    cache = api.new_cache(lay, 1, CTX_256K, dev)
+    c, s = W.int8_rows((1, shape.n_kv_heads, CTX_256K, D), 83, dev)
+    cache.codes().copy_(c)
+    cache.scales().copy_(s)
+    del c, s
+    q = W.normal((1, shape.n_q_heads, D), 83, "q_dec", torch.bfloat16, dev)
+    g_q = W.gains(D, 83, "g_q", False, torch.bfloat16, dev)
+    lens = torch.tensor([CTX_256K], dtype=torch.int32, device=dev)
+    out = api.gemma_attn_decode(lay, q, g_q, cache, None, lens, CTX_256K)
+    torch.cuda.synchronize()
+    rows = O.dequantize_rows(cache.codes().cpu().numpy(), cache.scales().cpu().numpy())
+    ref = O.decode_from_cache(oracle_layer(shape), to64(q), to64(g_q), rows, None, np.array([CTX_256K]))
+    assert_close(out, ref, torch.bfloat16, f"int8 decode at {CTX_256K} cached positions")
