@@ -33,12 +33,14 @@ from .attention import (  # noqa: F401
     OracleLayer,
     cache_bytes_per_token,
     decode_from_cache,
+    decode_from_prerotated_cache,
     decode_multi_from_cache,
     dequantize_rows,
     expected_caches_after_append,
     expected_caches_after_prefill,
     masked_softmax_attention,
     prefill,
+    prerotated_heads,
     qk_norm,
     quantize_rows,
     rope_frequencies,

@@ -355,6 +355,50 @@ def dequantize_rows(codes, scales) -> np.ndarray:
     return np.asarray(codes, dtype=np.float64) * _f64(scales)[..., None]
 
 
+# --- Pre-rotated ("1.25 d") global cache ---------------------------------------
+# The layout behind the pages' 37.5% figure (reading R12): per token, the
+# rotated leading 2 n_rot dims of the normalised key, plus the normalised,
+# unrotated d-dim row, which is the value and also supplies the key's remaining
+# dims.  It stores (1 + p) d values per token instead of the K=V tensor's d, and
+# needs no rotation when scores are formed.
+
+def prerotated_heads(layer: OracleLayer, rows, positions) -> np.ndarray:
+    """The cached heads of normalised, unrotated rows [..., P, d] at positions [P]:
+    their leading 2 n_rot dims rotated to their positions."""
+    n = 2 * rotated_pairs(layer.head_dim, layer.rope_fraction)
+    rotated = rotate(_f64(rows), np.asarray(positions), layer.rope_theta, layer.rope_fraction)
+    return rotated[..., :n]
+
+
+def decode_from_prerotated_cache(layer: OracleLayer, q, g_q, heads, rows, seq_lens,
+                                 batches=None) -> np.ndarray:
+    """One decode step per sequence against a pre-rotated global cache:
+    heads [B,Hkv,cap,2 n_rot] (rotated), rows [B,Hkv,cap,d] (unrotated).
+
+    Key j of KV head c is [heads[b,c,j], rows[b,c,j,2 n_rot:]], already at its
+    position; its value is rows[b,c,j].  q [B,Hq,d] raw at position L_b - 1.
+    Returns out [len(batches), Hq, d]."""
+    if not layer.kv_shared or layer.window:
+        raise ValueError("the pre-rotated cache is a global K=V layer layout")
+    G = layer.group
+    n = 2 * rotated_pairs(layer.head_dim, layer.rope_fraction)
+    batches = range(q.shape[0]) if batches is None else batches
+    out = []
+    for b in batches:
+        L = int(seq_lens[b])
+        qpos = np.array([L - 1])
+        q_rot = rotate(qk_norm(q[b], g_q, layer.norm_eps), L - 1, layer.rope_theta, layer.rope_fraction)
+        kpos = np.arange(L)
+        res = np.empty((layer.n_q_heads, layer.head_dim))
+        for c in range(layer.n_kv_heads):
+            vals = _f64(rows[b, c, :L])
+            keys = np.concatenate([_f64(heads[b, c, :L]), vals[:, n:]], axis=-1)
+            for h in range(c * G, (c + 1) * G):
+                res[h] = masked_softmax_attention(q_rot[h:h + 1], qpos, keys, vals, kpos, layer.scale, 0)[0]
+        out.append(res)
+    return np.stack(out)
+
+
 def cache_bytes_per_token(head_dim: int, fraction: float, layout: str,
                           bytes_per_elem: float = 1.0) -> float:
     """Bytes one KV head caches per token under three global-layer layouts.

@@ -445,3 +445,42 @@ def test_cache_layout_is_consistent_with_the_32k_memory_table(golden_dir):
     assert abs(total("shared") - target) / target < 0.02
     assert abs(total("prerotated") - target) / target > 0.1
     assert abs(total("separate") - target) / target > 0.5
+
+
+# ----------------------------------------------- pre-rotated ("1.25 d") cache ----
+
+def test_prerotated_heads_hand_values():
+    lay = layer(hq=2, hkv=1, d=8, kv_shared=True, theta=1e4, p=0.5)   # 2 rotated pairs: w0 = 1, w1 = 0.1
+    x = np.array([[1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0, 8.0]] * 2)
+    h = O.prerotated_heads(lay, x, [0, 2])
+    assert h.shape == (2, 4)
+    assert np.array_equal(h[0], x[0, :4])                                  # position 0: unrotated
+    c0, s0, c1, s1 = np.cos(2.0), np.sin(2.0), np.cos(0.2), np.sin(0.2)
+    want = [1 * c0 - 2 * s0, 1 * s0 + 2 * c0, 3 * c1 - 4 * s1, 3 * s1 + 4 * c1]
+    assert np.allclose(h[1], want, atol=1e-15)
+    # heads plus rows are the (1 + p) d values per token of the "prerotated" layout
+    lay512 = layer(hq=8, hkv=1, d=512, kv_shared=True, theta=1e6, p=0.25)
+    h512 = O.prerotated_heads(lay512, RNG.normal(size=(3, 512)), [0, 1, 2])
+    assert h512.shape[-1] + 512 == O.cache_bytes_per_token(512, 0.25, "prerotated")
+
+
+def test_prerotated_decode_equals_prefill_rows():
+    """Heads built at each slot's position from the K=V rows, read as keys
+    [head, row[2 n_rot:]] with the row as value: the prefill row again."""
+    d = 32
+    lay = layer(hq=8, hkv=2, d=d, kv_shared=True, theta=1e6, p=0.25)
+    B, T = 2, 13
+    q = RNG.normal(size=(B, T, lay.n_q_heads, d))
+    k = RNG.normal(size=(B, T, lay.n_kv_heads, d))
+    g_q = RNG.normal(1, 0.1, size=d)
+    g_k = RNG.normal(1, 0.1, size=d)
+    full = O.prefill(lay, q, k, None, g_q, g_k)
+    rows, _ = O.expected_caches_after_prefill(lay, k, None, g_k, T)
+    heads = O.prerotated_heads(lay, rows, np.arange(T))
+    for t in (0, 5, T - 1):
+        got = O.decode_from_prerotated_cache(lay, q[:, t], g_q, heads, rows, np.full(B, t + 1))
+        assert np.allclose(got, full[:, t], atol=1e-13)
+    # heads that were not rotated give other scores
+    wrong = O.decode_from_prerotated_cache(lay, q[:, T - 1], g_q, rows[..., :heads.shape[-1]], rows,
+                                           np.full(B, T))
+    assert not np.allclose(wrong, full[:, T - 1], atol=1e-6)
