@@ -46,6 +46,8 @@ MEASURED_TRAFFIC = {
                       "bytes": 4288964062},
     "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d8286757eaa8047a",
                             "bytes": 4312569210},
+    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "",
+                                 "bytes": 0},
     "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d8286757eaa8047a",
                            "bytes": 2173227349},
 }
@@ -80,6 +82,7 @@ def parse():
     ap.add_argument("--no-stack", action="store_true", help="skip the 6-layer stack decode leg")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode leg")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8-cache decode leg")
+    ap.add_argument("--no-prerotated", action="store_true", help="skip the pre-rotated-cache decode leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -370,6 +373,57 @@ def bench_int8_decode(args, torch, api, W):
     }
 
 
+def bench_prerotated_decode(args, torch, api, W):
+    """The global decode workload on a pre-rotated ("1.25 d") K=V cache: rows plus rotated heads."""
+    from dataclasses import replace
+    wl = W.CONFIGS["global_decode"]
+    shape = wl.layer
+    dev = torch.device("cuda", 0)
+    lens = wl.lengths()
+    B, cap, D = wl.batch, wl.cache_cap(), shape.head_dim
+    lay = replace(api.Layer.from_shape(shape, torch.bfloat16), cache_format=2)
+    cache = api.new_cache(lay, B, cap, dev)
+    for b in range(B):
+        cache.rows()[b:b + 1].copy_(W.normal((1, shape.n_kv_heads, cap, D), wl.seed + b, "k_cache",
+                                             torch.bfloat16, dev))
+        cache.heads()[b:b + 1].copy_(W.normal((1, shape.n_kv_heads, cap, cache.head_width), wl.seed + b, "k_new",
+                                              torch.bfloat16, dev))
+    q = W.normal((B, shape.n_q_heads, D), wl.seed, "q_dec", torch.bfloat16, dev)
+    g_q = W.gains(D, wl.seed, "g_q", False, torch.bfloat16, dev)
+    seq = lens.to(dev)
+    maxlen = int(lens.max())
+    out = torch.empty_like(q)
+    ws = api.workspace(api.gemma_attn_decode_workspace_size(lay, B, maxlen), dev)
+
+    def step():
+        api.gemma_attn_decode(lay, q, g_q, cache, None, seq, maxlen, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    sec = timed(step, args.decode_steps, 0, torch)
+    api.profile_enable(False)
+    split_ms, n_split = api.profile_read("decode_splitk")
+    api.profile_reset()
+    rows = int(lens.sum()) * shape.n_kv_heads
+    nbytes = rows * (D + cache.head_width) * 2     # each cached row and its head, once
+    del cache
+    torch.cuda.empty_cache()
+    split_ms /= max(n_split, 1)
+    return {
+        "workload": "global K=V layer decode on a pre-rotated cache (rows + rotated 128-dim heads, 1.25 d "
+                    "per row): B=16, context ~ U[4096,131072] (seed 0), 32q/4kv, d=512",
+        "value": round(nbytes / sec / 1e9, 1), "unit": "GB/s", "ms_per_step": round(sec * 1e3, 4),
+        "tokens_per_s": round(B / sec, 1), "kv_bytes": nbytes,
+        "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V,pre-rotated>", "bound": "hbm",
+                     "achieved": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4),
+                     "traffic": measured_traffic("prerotated_decode_splitk"), "avg_ms": round(split_ms, 4)},
+    }
+
+
 def bench_stack_decode(args, torch, api, W):
     """One decode step of a 6-layer stack (5 local + 1 global), each layer kv_append then decode."""
     wl_l, wl_g = W.CONFIGS["stack_decode_local"], W.CONFIGS["stack_decode_global"]
@@ -513,6 +567,11 @@ def main():
         }
     if not args.no_multi:
         line["multi_token_decode"] = bench_multi_decode(args, torch, api, W)
+    if not args.no_prerotated:
+        line["prerotated_decode"] = bench_prerotated_decode(args, torch, api, W)
+        if "decode" in line:
+            line["prerotated_decode"]["speedup_vs_kv_shared_cache"] = round(
+                line["decode"]["ms_per_step"] / line["prerotated_decode"]["ms_per_step"], 3)
     if not args.no_int8:
         line["int8_decode"] = bench_int8_decode(args, torch, api, W)
         if "decode" in line:

@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     GemmaAttnError,
     Int8Cache,
     Layer,
+    PrerotatedCache,
     cache_bytes,
     gemma_attn_decode,
     gemma_attn_decode_workspace_size,

@@ -8,7 +8,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemma_attn.so")
 
 GA_BF16, GA_F32 = 0, 1
-GA_CACHE_NATIVE, GA_CACHE_INT8 = 0, 1
+GA_CACHE_NATIVE, GA_CACHE_INT8, GA_CACHE_PREROTATED = 0, 1, 2
 STATUS = {0: "GA_OK", 1: "GA_EINVAL", 2: "GA_EUNSUPPORTED", 3: "GA_EWORKSPACE", 4: "GA_EHIP"}
 
 

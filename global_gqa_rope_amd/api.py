@@ -34,7 +34,7 @@ class Layer:
     norm_eps: float = 1e-6
     softmax_scale: float = 0.0     # <= 0: 1/sqrt(head_dim)
     dtype: torch.dtype = torch.bfloat16
-    cache_format: int = 0          # GA_CACHE_NATIVE; 1 = GA_CACHE_INT8 (global K=V layers, bf16)
+    cache_format: int = 0          # GA_CACHE_NATIVE; 1 = GA_CACHE_INT8, 2 = GA_CACHE_PREROTATED (global K=V, bf16)
 
     def struct(self) -> GaLayer:
         return GaLayer(self.n_q_heads, self.n_kv_heads, self.head_dim, self.window,
@@ -96,6 +96,32 @@ class Int8Cache:
         return self.buf[off:off + 4 * rows].view(torch.float32).view(self.batch, self.n_kv_heads, self.cap)
 
 
+@dataclass(frozen=True)
+class PrerotatedCache:
+    """A GA_CACHE_PREROTATED cache: one uint8 buffer of gemma_attn_cache_bytes
+    bytes holding the K=V rows and then each row's rotated head."""
+
+    buf: torch.Tensor
+    batch: int
+    cap: int
+    n_kv_heads: int
+    head_dim: int
+    head_width: int                # 2 n_rot
+    dtype: torch.dtype = torch.bfloat16
+
+    def rows(self) -> torch.Tensor:
+        """Normalised, unrotated rows [B, Hkv, cap, d] (a view)."""
+        n = self.batch * self.n_kv_heads * self.cap * self.head_dim
+        return self.buf[:n * 2].view(self.dtype).view(self.batch, self.n_kv_heads, self.cap, self.head_dim)
+
+    def heads(self) -> torch.Tensor:
+        """Rotated heads [B, Hkv, cap, 2 n_rot] (a view)."""
+        off = (self.batch * self.n_kv_heads * self.cap * self.head_dim * 2 + 255) // 256 * 256
+        n = self.batch * self.n_kv_heads * self.cap * self.head_width
+        return self.buf[off:off + 2 * n].view(self.dtype).view(self.batch, self.n_kv_heads, self.cap,
+                                                                 self.head_width)
+
+
 def cache_bytes(layer: Layer, batch: int, cap: int) -> int:
     n = int(_lib.load().gemma_attn_cache_bytes(ctypes.byref(layer.struct()), batch, cap))
     if n == 0 and batch > 0 and cap > 0:
@@ -108,6 +134,10 @@ def new_cache(layer: Layer, batch: int, cap: int, device):
     if layer.cache_format == _lib.GA_CACHE_INT8:
         buf = torch.zeros(cache_bytes(layer, batch, cap), dtype=torch.uint8, device=device)
         return Int8Cache(buf, batch, cap, layer.n_kv_heads, layer.head_dim)
+    if layer.cache_format == _lib.GA_CACHE_PREROTATED:
+        buf = torch.zeros(cache_bytes(layer, batch, cap), dtype=torch.uint8, device=device)
+        width = 2 * round(layer.head_dim * layer.rope_fraction / 2)
+        return PrerotatedCache(buf, batch, cap, layer.n_kv_heads, layer.head_dim, width, layer.dtype)
     return torch.zeros(batch, layer.n_kv_heads, cap, layer.head_dim, dtype=layer.dtype, device=device)
 
 
@@ -115,13 +145,14 @@ def _cache(layer: Layer, cache, name: str, batch: int) -> tuple[int | None, int]
     """(pointer, cache_cap) of a cache argument (None: (None, 0))."""
     if cache is None:
         return None, 0
-    if layer.cache_format == _lib.GA_CACHE_INT8:
-        if not isinstance(cache, Int8Cache):
-            raise ValueError(f"{name}: an int8-cache layer takes an Int8Cache")
+    if layer.cache_format in (_lib.GA_CACHE_INT8, _lib.GA_CACHE_PREROTATED):
+        kind = Int8Cache if layer.cache_format == _lib.GA_CACHE_INT8 else PrerotatedCache
+        if not isinstance(cache, kind):
+            raise ValueError(f"{name}: this layer's cache format takes a {kind.__name__}")
         if cache.batch != batch or cache.n_kv_heads != layer.n_kv_heads or cache.head_dim != layer.head_dim:
-            raise ValueError(f"{name}: Int8Cache made for another batch or layer")
+            raise ValueError(f"{name}: cache made for another batch or layer")
         if cache.buf.numel() < cache_bytes(layer, batch, cache.cap):
-            raise ValueError(f"{name}: Int8Cache buffer too small")
+            raise ValueError(f"{name}: cache buffer too small")
         return _ptr(cache.buf, name, dtype=torch.uint8), cache.cap
     cap = cache.shape[2]
     return _ptr(cache, name, layer, (batch, layer.n_kv_heads, cap, layer.head_dim)), cap

@@ -70,6 +70,7 @@ struct Derived {
   int n_rot;
   int elem;
   bool q8;                 // int8 K=V cache
+  bool pre;                // pre-rotated K=V cache (rows, then rotated heads)
   float scale;
   double log2_theta;
 };
@@ -94,8 +95,9 @@ ga_status check_layer(const ga_layer* L, Derived* out) {
   if (!(L->norm_eps > 0.f)) return fail(GA_EINVAL, "norm_eps must be > 0");
   if (!std::isfinite(L->softmax_scale)) return fail(GA_EINVAL, "softmax_scale must be finite");
   if (L->dtype != GA_BF16 && L->dtype != GA_F32) return fail(GA_EINVAL, "dtype must be GA_BF16 or GA_F32");
-  if (L->cache_format != GA_CACHE_NATIVE && L->cache_format != GA_CACHE_INT8)
-    return fail(GA_EINVAL, "cache_format must be GA_CACHE_NATIVE or GA_CACHE_INT8");
+  if (L->cache_format != GA_CACHE_NATIVE && L->cache_format != GA_CACHE_INT8 &&
+      L->cache_format != GA_CACHE_PREROTATED)
+    return fail(GA_EINVAL, "cache_format must be GA_CACHE_NATIVE, GA_CACHE_INT8 or GA_CACHE_PREROTATED");
 
   const int G = L->n_q_heads / L->n_kv_heads;
   const int n_rot = static_cast<int>(rounded);
@@ -111,11 +113,16 @@ ga_status check_layer(const ga_layer* L, Derived* out) {
       (!L->kv_shared || L->dtype != GA_BF16 || L->head_dim != 512 || (G != 4 && G != 8)))
     return fail(GA_EUNSUPPORTED, "the int8 cache is built for bf16 K=V layers with head_dim 512 and 4 or 8 "
                                  "query heads per KV head");
+  if (L->cache_format == GA_CACHE_PREROTATED &&
+      (!L->kv_shared || L->dtype != GA_BF16 || L->head_dim != 512 || (G != 4 && G != 8)))
+    return fail(GA_EUNSUPPORTED, "the pre-rotated cache is built for bf16 K=V layers with head_dim 512 and 4 or "
+                                 "8 query heads per KV head");
   if (out) {
     out->group = G;
     out->n_rot = n_rot;
     out->elem = L->dtype == GA_BF16 ? 2 : 4;
     out->q8 = L->cache_format == GA_CACHE_INT8;
+    out->pre = L->cache_format == GA_CACHE_PREROTATED;
     out->scale = L->softmax_scale > 0.f ? L->softmax_scale : 1.0f / std::sqrt(static_cast<float>(L->head_dim));
     out->log2_theta = std::log2(static_cast<double>(L->rope_theta));
   }
@@ -149,10 +156,20 @@ ga_status check_caches(const ga_layer* L, const void* k_cache, const void* v_cac
 size_t q8_scale_offset(const ga_layer* L, int batch, int cap) {
   return align_up(static_cast<size_t>(batch) * L->n_kv_heads * cap * L->head_dim);
 }
+// pre-rotated cache: rows [B][Hkv][cap][d] as the native K=V cache, then the
+// rotated heads [B][Hkv][cap][2 n_rot].
+size_t pre_heads_offset(const ga_layer* L, const Derived& dv, int batch, int cap) {
+  return align_up(static_cast<size_t>(batch) * L->n_kv_heads * cap * L->head_dim * dv.elem);
+}
 size_t cache_bytes(const ga_layer* L, const Derived& dv, int batch, int cap) {
   const size_t rows = static_cast<size_t>(batch) * L->n_kv_heads * cap;
   if (dv.q8) return q8_scale_offset(L, batch, cap) + rows * 4;
+  if (dv.pre) return pre_heads_offset(L, dv, batch, cap) + rows * 2 * dv.n_rot * dv.elem;
   return rows * L->head_dim * dv.elem;
+}
+void* pre_heads(const ga_layer* L, const Derived& dv, void* cache, int batch, int cap) {
+  if (!dv.pre || !cache) return nullptr;
+  return static_cast<char*>(cache) + pre_heads_offset(L, dv, batch, cap);
 }
 float* q8_scales(const ga_layer* L, const Derived& dv, void* cache, int batch, int cap) {
   if (!dv.q8 || !cache) return nullptr;
@@ -348,6 +365,7 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
       pa.window = layer->window; pa.kv_shared = layer->kv_shared; pa.cache_cap = cache_cap; pa.eps = layer->norm_eps;
       pa.pos0 = start;
       pa.k_scales = q8_scales(layer, dv, k_cache, batch, cache_cap);
+      pa.k_heads = pre_heads(layer, dv, k_cache, batch, cache_cap);
       st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "prefill prep launch");
     }
   }
@@ -409,6 +427,7 @@ ga_status kv_append(const ga_layer* layer, int32_t batch, const void* k_new, con
   aa.window = layer->window; aa.kv_shared = layer->kv_shared; aa.cache_cap = cache_cap; aa.eps = layer->norm_eps;
   aa.log2_theta = dv.log2_theta;
   aa.k_scales = q8_scales(layer, dv, k_cache, batch, cache_cap);
+  aa.k_heads = pre_heads(layer, dv, k_cache, batch, cache_cap);
   ProfScope ps(static_cast<hipStream_t>(stream), 4);
   return hip_status(ga::launch_kv_append(aa, layer->dtype, layer->head_dim, batch, static_cast<hipStream_t>(stream)),
                     "kv_append launch");
@@ -465,6 +484,7 @@ ga_status gemma_attn_decode_multi(const ga_layer* layer, int32_t batch, int32_t 
   da.window = layer->window; da.cache_cap = cache_cap; da.max_seq_len = max_seq_len; da.n_wgs = plan.n_wgs;
   da.q_len = q_len; da.slot_floats = static_cast<int>(plan.slot_floats);
   da.k_scales = q8_scales(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
+  da.k_heads = pre_heads(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
   da.eps = layer->norm_eps; da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
   return hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
                                       static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),

@@ -42,12 +42,18 @@ constexpr int kLdsLimit = 160 * 1024;
 // both formats, and the row scales are applied in fp32: to each score
 // (q . c s = (q . c) s) and to each softmax weight before it meets the codes
 // as values (p (c s) = (p s) c).
-template <typename T, int D, int G, bool SHARED, bool Q8 = false>
+// PRE: the pre-rotated ("1.25 d") K=V cache: the rows as in the native K=V
+// cache, plus per row its leading 2 n_rot dims already rotated to the row's
+// position (the heads).  The QK^T steps over those dims take the key operand
+// from the heads, loaded into registers a tile ahead, instead of rotating the
+// row's dims; nothing else changes.
+template <typename T, int D, int G, bool SHARED, bool Q8 = false, bool PRE = false>
 struct DecodeCfg {
   static constexpr int KT = 16;                       // keys per wave tile
   static constexpr int kD = D;
   static constexpr int kSz = int(sizeof(T));
-  static constexpr int kRot = SHARED ? 64 : 0;        // pairs rotated on the fly
+  static constexpr int kRot = (SHARED && !PRE) ? 64 : 0;   // pairs rotated on the fly
+  static constexpr int kHeadSteps = PRE ? 2 * 64 / 32 : 0;  // QK^T steps whose keys come from the heads
   static constexpr int kRotSteps = 2 * kRot / 32;     // QK^T steps that cover rotated dims
   static constexpr int kRowBytes = D * kSz;           // one key row
   static constexpr int kKBytes = KT * kRowBytes;      // key tile (the values too for K=V)
@@ -81,6 +87,7 @@ struct DecodeCfg {
   static_assert(kRowBytes / 16 >= 16, "row swizzle needs 16 chunks per row");
   static_assert(kTileBytes % 1024 == 0 && kDmaPerTile < 64, "tile copy");
   static_assert(!Q8 || (SHARED && sizeof(T) == 2 && kCodeBytes % 1024 == 0), "int8 tiles: bf16 K=V");
+  static_assert(!PRE || (SHARED && !Q8 && sizeof(T) == 2 && D == 512), "pre-rotated heads: bf16 K=V, d = 512");
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -272,7 +279,7 @@ struct QkStep {
 template <typename C, typename T>
 __device__ __forceinline__ void load_step(QkStep<T>& st, int u, uint32_t k_lane, uint32_t q_lane,
                                           uint32_t coarse_lane, uint32_t fine_lane) {
-  key_frag<C>(st.kf, k_lane, u);
+  if (u >= C::kHeadSteps) key_frag<C>(st.kf, k_lane, u);
   load_qfrag(st.qf, q_lane + u * C::kFragBytes);
   if (u < C::kRotSteps) {
 #pragma unroll
@@ -360,9 +367,9 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
   return x;
 }
 
-template <typename T, int D, int G, bool SHARED, bool Q8>
-__global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) void decode_kernel(DecodeArgs a) {
-  using C = DecodeCfg<T, D, G, SHARED, Q8>;
+template <typename T, int D, int G, bool SHARED, bool Q8, bool PRE>
+__global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64), 1) void decode_kernel(DecodeArgs a) {
+  using C = DecodeCfg<T, D, G, SHARED, Q8, PRE>;
   static_assert(C::KT == kDecodeTile, "tile size");
   const int kSlot = a.slot_floats;
   const int ncol = G * a.q_len;   // query columns: column c is token c / G, head c % G (<= 16)
@@ -431,6 +438,10 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) v
   // bytes of one head's cache rows: < 2^31 (checked on the host)
   const uint32_t span = static_cast<uint32_t>(a.cache_cap) * (Q8 ? C::kD : C::kRowBytes);
   Seg pf = cur;
+  // PRE: the lane's head fragments (row hcol, dims 32u + 8kg .. +7, u < 4) of
+  // the tile whose copy was issued last
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 head_next[C::kHeadSteps > 0 ? C::kHeadSteps : 1];
   auto issue = [&](lds_char* dst, int k) {
     const int g = t_begin + wave + C::kWaves * k;
     if (g >= t_end) return;
@@ -443,6 +454,15 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) v
     } else {
       const BufRsrc rv = SHARED ? rk : make_rsrc(static_cast<const char*>(a.v_cache) + head * span, span);
       issue_tile<C>(dst, rk, rv, (g - pf.T) * C::KT, pf.keys, lane);
+    }
+    if constexpr (PRE) {   // rows past the sequence read its last row, like the tile
+      constexpr uint32_t kHeadRow = 2 * 64 * sizeof(T);
+      const BufRsrc rh = make_rsrc(static_cast<const char*>(a.k_heads) + head * a.cache_cap * kHeadRow,
+                                   static_cast<uint32_t>(a.cache_cap) * kHeadRow);
+      const int key = min((g - pf.T) * C::KT + (lane & 15), pf.keys - 1);
+#pragma unroll
+      for (int u = 0; u < C::kHeadSteps; ++u)
+        head_next[u] = __builtin_amdgcn_raw_buffer_load_b128(rh, key * kHeadRow + (32 * u + 8 * (lane >> 4)) * 2, 0, 0);
     }
   };
   issue(Q8 ? stage_buf : tile_buf, 0);
@@ -466,7 +486,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) v
   // few 1e-6.
   f32x2 coarse_l{}, step_l{};
   const uint32_t coarse_s = smem0 + C::kCoarseOff + wave * C::kCoarseBytes;
-  if constexpr (SHARED) {
+  if constexpr (C::kRot > 0) {
     static_assert(kThreads % 64 == 0 && C::kRot == 64, "fine table: thread t fills pair t % 64");
     for (int i = threadIdx.x; i < 16 * C::kRot; i += kThreads) {
       float sn, cs;
@@ -550,7 +570,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) v
         }
       }
     }
-    if constexpr (SHARED) {   // coarse angles of the wave's first tile in this segment
+    if constexpr (C::kRot > 0) {   // coarse angles of the wave's first tile in this segment
       const int g = t_begin + wave + C::kWaves * k;
       coarse_l = rope_cos_sin(static_cast<double>((g - cur.T) * C::KT) * w_pair[0]);
       lds_st<f32x2>(coarse_s + lane * 8, coarse_l);
@@ -576,6 +596,11 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) v
       // them.
       auto step = [&](lds_char* __restrict__ cur_buf, lds_char* __restrict__ nxt,
                       const lds_char* __restrict__ stage) {
+        u32x4 head_cur[C::kHeadSteps > 0 ? C::kHeadSteps : 1];   // PRE: tile k's heads (landed with it)
+        if constexpr (PRE) {
+  #pragma unroll
+          for (int u = 0; u < C::kHeadSteps; ++u) head_cur[u] = head_next[u];
+        }
         issue(nxt, k + 1);
         if constexpr (Q8) {
           expand_q8<C>(stage, cur_buf, lane);
@@ -593,6 +618,9 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) v
           if (u + kQAhead < C::kQSteps)
             load_step<C>(st[(u + kQAhead) % (kQAhead + 1)], u + kQAhead, k_lane + buf, q_lane, coarse_lane, fine_lane);
           QkStep<T>& cs = st[u % (kQAhead + 1)];
+          if constexpr (PRE) {
+            if (u < C::kHeadSteps) cs.kf.v = __builtin_bit_cast(bf16x8, head_cur[u]);
+          }
           if (u < C::kRotSteps) rotate_step(cs);
           mma16((u & 1) ? sb : sa, cs.kf, cs.qf);
           __builtin_amdgcn_sched_barrier(0);
@@ -603,7 +631,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8>::kWaves * 64), 1) v
           row_scale = *(const __attribute__((address_space(3))) f32x4*)(stage + C::kCodeBytes + 16 * kg);
           s *= row_scale;
         }
-        if constexpr (SHARED) {   // publish the wave's next tile's coarse angles
+        if constexpr (C::kRot > 0) {   // publish the wave's next tile's coarse angles
           const f32x2 c = coarse_l;
           coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
           coarse_l[1] = c[1] * step_l[0] + c[0] * step_l[1];
@@ -749,11 +777,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
-template <typename T, int D, int G, bool SHARED, bool Q8 = false>
+template <typename T, int D, int G, bool SHARED, bool Q8 = false, bool PRE = false>
 static hipError_t launch_one(const DecodeArgs& a, hipStream_t s, LaunchTimer timer) {
-  using C = DecodeCfg<T, D, G, SHARED, Q8>;
+  using C = DecodeCfg<T, D, G, SHARED, Q8, PRE>;
   if (timer) timer(s, 2, true);
-  hipLaunchKernelGGL((decode_kernel<T, D, G, SHARED, Q8>), dim3(a.n_wgs), dim3(C::kWaves * 64), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, SHARED, Q8, PRE>), dim3(a.n_wgs), dim3(C::kWaves * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (timer) timer(s, 2, false);
   if (e != hipSuccess) return e;
@@ -768,8 +796,17 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t s, LaunchTimer tim
 template <typename T, int D, bool SHARED>
 static hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t s, LaunchTimer tm) {
   if constexpr (SHARED && D == 512 && sizeof(T) == 2) {
-    static_assert(DecodeCfg<T, D, 8, SHARED, true>::kWaves == DecodeCfg<T, D, 8, SHARED>::kWaves,
-                  "the plan and the merge assume one wave count for both cache formats");
+    static_assert(DecodeCfg<T, D, 8, SHARED, true>::kWaves == DecodeCfg<T, D, 8, SHARED>::kWaves &&
+                      DecodeCfg<T, D, 8, SHARED, false, true>::kWaves == DecodeCfg<T, D, 8, SHARED>::kWaves,
+                  "the plan and the merge assume one wave count for every cache format");
+    if (a.k_heads) {   // pre-rotated K=V cache
+      if (a.k_scales) return hipErrorInvalidValue;
+      switch (group) {
+        case 8: return launch_one<T, D, 8, SHARED, false, true>(a, s, tm);
+        case 4: return launch_one<T, D, 4, SHARED, false, true>(a, s, tm);
+        default: return hipErrorInvalidValue;
+      }
+    }
     if (a.k_scales) {   // int8 K=V cache
       switch (group) {
         case 8: return launch_one<T, D, 8, SHARED, true>(a, s, tm);
@@ -778,7 +815,7 @@ static hipError_t launch_g(const DecodeArgs& a, int group, hipStream_t s, Launch
       }
     }
   }
-  if (a.k_scales) return hipErrorInvalidValue;
+  if (a.k_scales || a.k_heads) return hipErrorInvalidValue;
   switch (group) {
     case 1: return launch_one<T, D, 1, SHARED>(a, s, tm);
     case 2: return launch_one<T, D, 2, SHARED>(a, s, tm);

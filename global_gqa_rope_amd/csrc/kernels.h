@@ -34,6 +34,7 @@ struct PrepArgs {
   int seq_len, seq_pad, n_kv_heads, n_rot, window, kv_shared, cache_cap, kw;
   int pos0;                // position of k's first row; rows 0 .. pos0-1 come from the K=V cache
   float* k_scales;         // int8 K=V cache: per-row scales [B][Hkv][cache_cap] (else null)
+  void* k_heads;           // pre-rotated K=V cache: heads [B][Hkv][cache_cap][2 n_rot] (else null)
   float eps;
 };
 
@@ -46,6 +47,7 @@ struct AppendArgs {
   void* v_cache;
   int n_kv_heads, n_rot, window, kv_shared, cache_cap;
   float* k_scales;         // int8 K=V cache: per-row scales (else null)
+  void* k_heads;           // pre-rotated K=V cache: heads (else null)
   float eps;
   double log2_theta;
 };
@@ -75,6 +77,7 @@ struct DecodeArgs {
   int batch, n_q_heads, n_kv_heads, n_rot, window, cache_cap, max_seq_len;
   int q_len;               // query tokens per sequence: the last q_len positions (1 = one token)
   const float* k_scales;   // int8 K=V cache: per-row scales [B][Hkv][cache_cap] (else null)
+  const void* k_heads;     // pre-rotated K=V cache: heads [B][Hkv][cache_cap][2 n_rot] (else null)
   int slot_floats;         // q_len * G * D + 64
   int n_wgs;               // split-K workgroups (the grid)
   float eps;

@@ -180,6 +180,17 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
     }
   }
 
+  // Pre-rotated K=V caches also keep each new row's rotated head
+  // (dims 0 .. 2 n_rot - 1, as the key row above).
+  if (a.k_heads && valid) {
+    T* __restrict__ hk = static_cast<T*>(a.k_heads) + (head_base * a.cache_cap + pos) * (2 * a.n_rot);
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int d0 = (i * 8 + c8) * 8;
+      if (d0 < 2 * a.n_rot) *reinterpret_cast<vec8*>(hk + d0) = kout[i];
+    }
+  }
+
   // Separate-V layers: windowed ones keep the last W positions in a ring of
   // cache_cap = W slots, global ones every position (slot = position); keys
   // rotated.
@@ -241,6 +252,20 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
     else *reinterpret_cast<uint32_t*>(codes) = u.x;
     if (l == 0) a.k_scales[head_base * a.cache_cap + slot] = sc;
     return;
+  }
+  if (a.k_heads && l * kPer < 2 * a.n_rot) {   // pre-rotated K=V cache: the row's rotated head too
+    float r[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) r[j] = x[j];
+#pragma unroll
+    for (int j = 0; j < kPer / 2; ++j) {
+      const int pair = l * kPer / 2 + j;
+      if (pair < a.n_rot)
+        rotate_pair(r[2 * j], r[2 * j + 1], rope_cos_sin(static_cast<double>(pos) * rope_omega(pair, D, a.log2_theta)));
+    }
+    T* __restrict__ hk = static_cast<T*>(a.k_heads) + (head_base * a.cache_cap + slot) * (2 * a.n_rot) + l * kPer;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) hk[j] = from_f32<T>(r[j]);
   }
   T* __restrict__ kc = static_cast<T*>(a.k_cache) + (head_base * a.cache_cap + slot) * D + l * kPer;
   if (!a.kv_shared) {

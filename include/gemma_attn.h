@@ -101,7 +101,20 @@ typedef struct {
  * writes the cache; decode and a later prefill chunk read cached rows back as
  * c_i * s.  Decode streams about half the bytes of a bf16 cache.
  */
-typedef enum { GA_CACHE_NATIVE = 0, GA_CACHE_INT8 = 1 } ga_cache_format;
+/*
+ * GA_CACHE_PREROTATED (the same layers as GA_CACHE_INT8) is the "1.25 d"
+ * layout the pages' 37.5% reduction describes ("解读 Gemma 4 的架构创新",
+ * "关键架构创新" ② Keys as Values; "Gemma 4 Technical Report" notes, §2): per
+ * cached row, the normalised unrotated key, which is also the value, plus its
+ * leading 2 n_rot dims already rotated to the row's position.  One k_cache
+ * buffer holds, in dtype elements:
+ *   [B][Hkv][cache_cap][d]         the rows, laid out as a GA_CACHE_NATIVE K=V cache
+ *   then, at byte offset round_up(B * Hkv * cache_cap * d * sizeof(dtype), 256),
+ *   [B][Hkv][cache_cap][2 n_rot]   the rotated heads
+ * Decode takes the rotated dims of each key from the heads instead of rotating
+ * them; it reads 1.25 d values per cached row instead of d.
+ */
+typedef enum { GA_CACHE_NATIVE = 0, GA_CACHE_INT8 = 1, GA_CACHE_PREROTATED = 2 } ga_cache_format;
 
 /* Bytes of one cache tensor (k_cache; v_cache alike) of this layer. */
 size_t gemma_attn_cache_bytes(const ga_layer* layer, int32_t batch, int32_t cache_cap);

@@ -64,7 +64,9 @@ def prefill(lib, layer, B=1, S=16, v=None, k_cache=None, v_cache=None, cap=0, ws
     (L(hq=48, hkv=3), 2, "1, 2, 4, 8"),
     (L(window=64), 2, "window 0"),
     (L(p=0.5), 2, "64 pairs"),
-    (L(cache=2), 1, "cache_format"),
+    (L(cache=3), 1, "cache_format"),
+    (L(cache=2, dtype=1), 2, "pre-rotated cache"),
+    (L(cache=2, hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0), 2, "pre-rotated cache"),
     (L(cache=1, dtype=1), 2, "int8 cache"),
     (L(cache=1, hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0), 2, "int8 cache"),
     (L(cache=1, hq=8, hkv=4), 2, "int8 cache"),
@@ -185,6 +187,10 @@ def test_cache_bytes(lib):
     e = L(hq=8, hkv=2, cache=1)
     codes = 3 * 2 * 7 * 512
     assert lib.gemma_attn_cache_bytes(ctypes.byref(e), 3, 7) == -(-codes // 256) * 256 + 3 * 2 * 7 * 4
+    pre = L(cache=2)
+    # rows [B,Hkv,cap,d] bf16 (the native K=V cache), then heads [B,Hkv,cap,2 n_rot] bf16
+    rows = 2 * 4 * 100 * 512 * 2
+    assert lib.gemma_attn_cache_bytes(ctypes.byref(pre), 2, 100) == -(-rows // 256) * 256 + 2 * 4 * 100 * 128 * 2
     assert lib.gemma_attn_cache_bytes(ctypes.byref(L(cache=5)), 1, 1) == 0   # invalid layer
 
 
