@@ -202,3 +202,34 @@ def test_int8_cache_alignment_is_checked(lib):
     pos = FAKE
     st = lib.kv_append(ctypes.byref(q8), 1, FAKE, None, FAKE, pos, odd, None, 64, None)
     assert st == 1 and "16-byte" in lib.gemma_attn_last_error().decode()
+
+
+def test_binding_checks_cache_formats():
+    """The torch binding rejects a cache of the wrong kind before any call."""
+    from dataclasses import replace
+
+    import torch
+
+    from global_gqa_rope_amd import api
+    from global_gqa_rope_amd import workloads as W
+
+    base = api.Layer.from_shape(W.GLOBAL_LAYER, torch.bfloat16)
+    q8, pre = replace(base, cache_format=1), replace(base, cache_format=2)
+    q = torch.zeros(2, 32, 512, dtype=torch.bfloat16)
+    plain = torch.zeros(2, 4, 16, 512, dtype=torch.bfloat16)
+    for lay, kind in ((q8, "Int8Cache"), (pre, "PrerotatedCache")):
+        with pytest.raises(ValueError, match=kind):
+            api.gemma_attn_decode(lay, q, q[0, 0], plain, None, torch.zeros(2, dtype=torch.int32), 16)
+    c8 = api.new_cache(q8, 2, 16, "cpu")
+    cp = api.new_cache(pre, 2, 16, "cpu")
+    assert c8.buf.numel() == api.cache_bytes(q8, 2, 16) and cp.buf.numel() == api.cache_bytes(pre, 2, 16)
+    assert cp.rows().shape == (2, 4, 16, 512) and cp.heads().shape == (2, 4, 16, 128)
+    with pytest.raises(ValueError, match="Int8Cache"):
+        api.gemma_attn_decode(q8, q, q[0, 0], cp, None, torch.zeros(2, dtype=torch.int32), 16)
+    with pytest.raises(ValueError, match="another batch"):          # made for B=2, used with B=3
+        api.gemma_attn_decode(q8, torch.zeros(3, 32, 512, dtype=torch.bfloat16), q[0, 0], c8, None,
+                              torch.zeros(3, dtype=torch.int32), 16)
+    with pytest.raises(ValueError, match="device tensor"):           # the binding only passes device memory
+        api.gemma_attn_decode(q8, q, q[0, 0], c8, None, torch.zeros(2, dtype=torch.int32), 16)
+    with pytest.raises(api.GemmaAttnError, match="int8 cache"):      # no int8 cache for local layers
+        api.new_cache(replace(api.Layer.from_shape(W.LOCAL_LAYER, torch.bfloat16), cache_format=1), 1, 8, "cpu")
