@@ -353,6 +353,11 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  // Separate-V layers: the attention kernel reads v in place when one head's
+  // rows (Hkv d elements apart) span less than 2^31 bytes; else prep copies it
+  // into the workspace rows.
+  const bool v_in_place = !layer->kv_shared &&
+      static_cast<int64_t>(seq_len) * layer->n_kv_heads * layer->head_dim * dv.elem < (int64_t{1} << 31);
   {
     ProfScope ps(s, 1);
     st = hip_status(ga::launch_rope_table(ws + lay.table, lay.seq_pad, dv.n_rot, layer->head_dim, dv.log2_theta, s),
@@ -364,6 +369,7 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
       pa.seq_len = seq_len; pa.seq_pad = lay.seq_pad; pa.n_kv_heads = layer->n_kv_heads; pa.n_rot = dv.n_rot;
       pa.window = layer->window; pa.kv_shared = layer->kv_shared; pa.cache_cap = cache_cap; pa.eps = layer->norm_eps;
       pa.pos0 = start;
+      pa.write_v = !layer->kv_shared && !v_in_place;
       pa.k_scales = q8_scales(layer, dv, k_cache, batch, cache_cap);
       pa.k_heads = pre_heads(layer, dv, k_cache, batch, cache_cap);
       st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "prefill prep launch");
@@ -376,6 +382,7 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
   fa.out = out; fa.seq_len = seq_len; fa.seq_pad = lay.seq_pad; fa.n_q_heads = layer->n_q_heads;
   fa.n_kv_heads = layer->n_kv_heads; fa.n_rot = dv.n_rot; fa.window = layer->window; fa.eps = layer->norm_eps;
   fa.q_pos0 = start;
+  fa.v = v_in_place ? v : nullptr;
   fa.qk_scale_log2 = dv.scale * 1.4426950408889634f;
   ProfScope ps(s, 0);
   return hip_status(ga::launch_prefill_attn(fa, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch, s),

@@ -33,6 +33,7 @@ struct PrepArgs {
   void* ws_v;              // [B][Hkv][seq_pad][d] value rows
   int seq_len, seq_pad, n_kv_heads, n_rot, window, kv_shared, cache_cap, kw;
   int pos0;                // position of k's first row; rows 0 .. pos0-1 come from the K=V cache
+  int write_v;             // separate-V layers: copy v into ws_v (the attention kernel reads it there)
   float* k_scales;         // int8 K=V cache: per-row scales [B][Hkv][cache_cap] (else null)
   void* k_heads;           // pre-rotated K=V cache: heads [B][Hkv][cache_cap][2 n_rot] (else null)
   float eps;
@@ -57,7 +58,8 @@ struct PrefillArgs {
   const void* q_gain;
   const void* rope_table;
   const void* ws_k;        // see PrepArgs
-  const void* ws_v;
+  const void* ws_v;        // K=V layers' value rows (separate-V layers read v)
+  const void* v;           // separate-V layers: v [B][S][Hkv][d] read in place (null: ws_v holds it)
   void* out;
   int seq_len, seq_pad, n_q_heads, n_kv_heads, n_rot, window;
   int q_pos0;              // position of q's (and out's) first row; keys from position 0

@@ -53,6 +53,7 @@ struct PrefillCfg {
   static constexpr int kQSteps = D / 16;            // QK^T reduction steps
   static constexpr int kDBlocks = D / 32;           // 32-dim output blocks
   static constexpr int kSz = int(sizeof(T));
+  static constexpr bool kShared = SHARED;
   static constexpr int kKW = SHARED ? 128 : D;      // key dims staged from the key rows
   static constexpr int kKSteps = kKW / 16;          // QK^T steps reading the key rows
   static constexpr int kKRowBytes = kKW * kSz;
@@ -179,12 +180,16 @@ __device__ __forceinline__ int row_swizzle(int r) { return ((r & 3) << 2) | ((r 
 // w, w + kWaves, ...; copy_piece gives the k-th of them.
 struct CopyPiece {
   bool is_k;     // key region (else value region)
-  int rb;        // row bytes of that region
+  int rb;        // row bytes of that region in LDS
+  int gs;        // bytes between consecutive rows of that region in global memory
   int lds;       // LDS offset of the instruction within the stage
   int voff;      // byte offset within the tile's rows in global memory
 };
+// vstride: bytes between consecutive value rows in global memory.  K=V layers
+// stage the workspace's value rows (kVRowBytes apart, a compile-time
+// constant); layers with a separate V read v where it lies, token-major.
 template <typename C>
-__device__ __forceinline__ CopyPiece copy_piece(int k, int wave, int lane) {
+__device__ __forceinline__ CopyPiece copy_piece(int k, int wave, int lane, uint32_t vstride) {
   static_assert(C::kDmaK % C::kWaves == 0, "key-region instructions split evenly over the waves");
   constexpr int kPerWaveK = C::kDmaK / C::kWaves;
   CopyPiece cp;
@@ -192,6 +197,7 @@ __device__ __forceinline__ CopyPiece copy_piece(int k, int wave, int lane) {
   const int j = (cp.is_k ? k : k - kPerWaveK) * C::kWaves + wave;   // piece within its region
   const int i = (cp.is_k ? 0 : C::kDmaK) + j;               // = k kWaves + wave
   cp.rb = cp.is_k ? C::kKRowBytes : C::kVRowBytes;
+  cp.gs = cp.is_k ? C::kKRowBytes : (C::kShared ? C::kVRowBytes : static_cast<int>(vstride));
   int r, slot;
   if (cp.rb >= 1024) {
     r = j / (cp.rb / 1024);
@@ -201,15 +207,29 @@ __device__ __forceinline__ CopyPiece copy_piece(int k, int wave, int lane) {
     slot = lane % (cp.rb / 16);
   }
   cp.lds = i * 1024;
-  cp.voff = r * cp.rb + ((slot ^ row_swizzle(r)) << 4);
+  cp.voff = r * cp.gs + ((slot ^ row_swizzle(r)) << 4);
   return cp;
 }
+// One copy instruction of a tile.  The tile's first row goes into the scalar
+// offset, which the buffer's range check does not cover, except for values
+// read in place (separate-V layers): there the whole offset is in the checked
+// per-lane offset, so the rows past the sequence in its last tile read zeros
+// instead of memory past v.
 template <typename C>
-__device__ __forceinline__ void issue_tile(BufRsrc rk, BufRsrc rv, int tile, lds_char* dst, int wave, int lane) {
+__device__ __forceinline__ void copy_load(const CopyPiece& cp, BufRsrc rk, BufRsrc rv, lds_char* dst, int tile) {
+  const uint32_t tile_off = static_cast<uint32_t>(tile) * C::KT * cp.gs;
+  if (!C::kShared && !cp.is_k)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst + cp.lds, 16, cp.voff + tile_off, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.is_k ? rk : rv, dst + cp.lds, 16, cp.voff, tile_off, 0, 0);
+}
+template <typename C>
+__device__ __forceinline__ void issue_tile(BufRsrc rk, BufRsrc rv, uint32_t vstride, int tile, lds_char* dst, int wave,
+                                           int lane) {
 #pragma unroll
   for (int k = 0; k < C::kDmaPerWave; ++k) {
-    const CopyPiece cp = copy_piece<C>(k, wave, lane);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.is_k ? rk : rv, dst + cp.lds, 16, cp.voff, tile * C::KT * cp.rb, 0, 0);
+    const CopyPiece cp = copy_piece<C>(k, wave, lane, vstride);
+    copy_load<C>(cp, rk, rv, dst, tile);
   }
 }
 
@@ -440,17 +460,19 @@ __device__ __forceinline__ void pv_tile(const lds_char* st, const LaneOffsets& l
 template <typename C>
 struct TileCopier {
   BufRsrc rk, rv;
+  uint32_t vstride;
   lds_char* nxt;
   int tile, wave, ln;
   __device__ __forceinline__ void operator()(int k) const {
-    const CopyPiece cp = copy_piece<C>(k, wave, ln);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(cp.is_k ? rk : rv, nxt + cp.lds, 16, cp.voff, tile * C::KT * cp.rb, 0, 0);
+    const CopyPiece cp = copy_piece<C>(k, wave, ln, vstride);
+    copy_load<C>(cp, rk, rv, nxt, tile);
   }
 };
 template <typename C>
 __device__ __forceinline__ TileCopier<C> make_copier(const char* kbase, const char* vbase, uint32_t kspan,
-                                                     uint32_t vspan, lds_char* nxt, int tile, int wave, int lane) {
-  return TileCopier<C>{make_rsrc(kbase, kspan), make_rsrc(vbase, vspan), nxt, tile, wave, lane};
+                                                     uint32_t vspan, uint32_t vstride, lds_char* nxt, int tile,
+                                                     int wave, int lane) {
+  return TileCopier<C>{make_rsrc(kbase, kspan), make_rsrc(vbase, vspan), vstride, nxt, tile, wave, lane};
 }
 
 // One whole tile (fewer than three stages): QK^T, softmax and PV from `cur`,
@@ -462,11 +484,11 @@ __device__ __forceinline__ TileCopier<C> make_copier(const char* kbase, const ch
 template <typename C, typename T, int D, bool MASK>
 __device__ __forceinline__ void tile_step(const lds_char* __restrict__ cur, lds_char* __restrict__ nxt,
                                           const char* kbase, const char* vbase, uint32_t kspan, uint32_t vspan,
-                                          int next_tile, int wave, int lane, const LaneOffsets& lo,
+                                          uint32_t vstride, int next_tile, int wave, int lane, const LaneOffsets& lo,
                                           const QSource<T, D>& qs, int key0, int pos, int window,
                                           RowState<C::kDBlocks>& rs) {
   const int h = lane >> 5;
-  const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, nxt, next_tile, wave, lane);
+  const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, vstride, nxt, next_tile, wave, lane);
   f32x16 s;
   Frag8<T> kf[C::kKAhead];
   qk_prefetch<C, T, D>(kf, cur, lo);
@@ -491,7 +513,8 @@ __device__ __forceinline__ void tile_step(const lds_char* __restrict__ cur, lds_
 template <typename C, typename T, int D, bool MASK, bool NEXT>
 __device__ __forceinline__ void pipe_step(const lds_char* __restrict__ kcur, const lds_char* __restrict__ vcur,
                                           lds_char* __restrict__ nxt, const char* kbase, const char* vbase,
-                                          uint32_t kspan, uint32_t vspan, int next_tile, int wave, int lane,
+                                          uint32_t kspan, uint32_t vspan, uint32_t vstride, int next_tile, int wave,
+                                          int lane,
                                           const LaneOffsets& lo, const QSource<T, D>& qs, int key0, int pos,
                                           int window, RowState<C::kDBlocks>& rs, f32x16& s) {
   const int h = lane >> 5;
@@ -505,7 +528,7 @@ __device__ __forceinline__ void pipe_step(const lds_char* __restrict__ kcur, con
   Frag8<T> pf[2];
   if constexpr (NEXT) {
     // exponential r after QK^T MFMA r
-    const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, nxt, next_tile, wave, lane);
+    const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, vstride, nxt, next_tile, wave, lane);
     qk_run<C, T, D, C::kDmaPerWave>(s, kf, kcur, lo, qs, h, copy, [&](int u) {
       if (u < 16) {
         const float p = __builtin_amdgcn_exp2f(sv[u] - m_use);
@@ -565,14 +588,27 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const int kt_hi = p_last / C::KT + 1;
   const int64_t head = static_cast<int64_t>(b) * a.n_kv_heads + kvh;
   const char* kbase = static_cast<const char*>(a.ws_k) + head * a.seq_pad * C::kKRowBytes;
-  const char* vbase = static_cast<const char*>(a.ws_v) + head * a.seq_pad * C::kVRowBytes;
+  // Value rows: the workspace's (K=V layers, and separate-V layers whose
+  // rows of one head span 2^31 bytes or more), or v itself, token-major, rows
+  // Hkv d apart (the other separate-V layers).  Rows past the sequence read
+  // zeros (the buffer's range check; see copy_load).
+  const char* vbase;
+  uint32_t vspan, vstride;
+  if (C::kShared || a.v == nullptr) {
+    vbase = static_cast<const char*>(a.ws_v) + head * a.seq_pad * C::kVRowBytes;
+    vspan = static_cast<uint32_t>(a.seq_pad) * C::kVRowBytes;
+    vstride = C::kVRowBytes;
+  } else {
+    vstride = static_cast<uint32_t>(a.n_kv_heads) * C::kVRowBytes;
+    vbase = static_cast<const char*>(a.v) + (static_cast<int64_t>(b) * a.seq_len * a.n_kv_heads + kvh) * C::kVRowBytes;
+    vspan = static_cast<uint32_t>(a.seq_len - 1) * vstride + C::kVRowBytes;
+  }
   const uint32_t kspan = static_cast<uint32_t>(a.seq_pad) * C::kKRowBytes;   // < 2^31 (host check)
-  const uint32_t vspan = static_cast<uint32_t>(a.seq_pad) * C::kVRowBytes;
   const BufRsrc rk = make_rsrc(kbase, kspan);
   const BufRsrc rv = make_rsrc(vbase, vspan);
 #pragma unroll
   for (int i = 0; i < C::kStages - 1; ++i)
-    issue_tile<C>(rk, rv, kt_lo + i, (lds_char*)smem + i * C::kStageBytes, wave, lane);
+    issue_tile<C>(rk, rv, vstride, kt_lo + i, (lds_char*)smem + i * C::kStageBytes, wave, lane);
 
   // ---- prologue: QKNorm + rotation of query row m (this lane's half) ---------
   // bf16: the query fragments stay in registers.  fp32 would need 256
@@ -696,7 +732,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       asm volatile("" ::: "memory");
       pipe_step<C, T, D, decltype(masked)::value, true>(
           stage_of(kt + 1), stage_of(kt), stage_of(kt + C::kStages - 1), kbase, vbase, kspan, vspan,
-          kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos, a.window, st, s);
+          vstride, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos, a.window, st, s);
     };
     const int last = kt_hi - 1;
     const int m1 = min(lo_end, last), m2 = max(m1, min(hi_begin, last));
@@ -711,7 +747,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     // The last tile (always an edge): its values landed with its keys, and
     // nothing is copied, so neither a wait nor a barrier.
     pipe_step<C, T, D, true, false>(stage_of(last + 1), stage_of(last), stage_of(last + C::kStages - 1), kbase,
-                                    vbase, kspan, vspan, 0, wave, lane, lo, qs, last * C::KT, pos, a.window, st, s);
+                                    vbase, kspan, vspan, vstride, 0, wave, lane, lo, qs, last * C::KT, pos, a.window, st, s);
   } else {
     // One tile per step: wait for it, barrier, then the (masked or plain) step.
     auto run_tile = [&](int kt, auto masked) {
@@ -723,12 +759,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       tile_step<C, T, D, decltype(masked)::value>(stage_of(kt), stage_of(kt + C::kStages - 1), kbase, vbase, kspan,
-                                                  vspan, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos,
+                                                  vspan, vstride, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos,
                                                   a.window, st);
       if (C::kStages == 1 && kt + 1 < kt_hi) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue_tile<C>(rk, rv, kt + 1, lds, wave, lane);
+        issue_tile<C>(rk, rv, vstride, kt + 1, lds, wave, lane);
       }
     };
     int kt = kt_lo;

@@ -60,6 +60,10 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   const int64_t src_row = ((static_cast<int64_t>(b) * a.seq_len + src_pos) * a.n_kv_heads + h) * D;
   const bool has_v = !a.kv_shared;
   const int64_t head_base = (static_cast<int64_t>(b) * a.n_kv_heads + h);
+  // separate-V layers: the row goes to the caches (windowed: the last W positions)
+  const bool v_to_cache = has_v && a.k_cache && valid && (a.window == 0 || pos >= a.seq_len - a.window);
+  // v is read where it is copied: ws_v (when the attention kernel reads it there) or the caches
+  const bool need_v = has_v && (a.write_v || v_to_cache);
 
   const T* __restrict__ k = static_cast<const T*>(a.k);
   const T* __restrict__ v = static_cast<const T*>(a.v);
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
     if (cached && q8) qin[i] = *reinterpret_cast<const uint2*>(code_row + d0);
     else kin[i] = *reinterpret_cast<const vec8*>((cached ? cache_row : k + src_row) + d0);
     gin[i] = *reinterpret_cast<const vec8*>(gk + d0);
-    if (has_v) vin[i] = *reinterpret_cast<const vec8*>(v + src_row + d0);
+    if (need_v) vin[i] = *reinterpret_cast<const vec8*>(v + src_row + d0);
   }
   if (cached && q8) q_scale = a.k_scales[head_base * a.cache_cap + pos];
   // (cos, sin) of the chunk's four pairs; pairs >= n_rot read a clamped entry
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
       for (int j = 0; j < 8; ++j) vout[i][j] = from_f32<T>(x[i][j]);
       if (kc && valid && !q8) *reinterpret_cast<vec8*>(kc + (head_base * a.cache_cap + pos) * D + d0) = vout[i];
     }
-    *reinterpret_cast<vec8*>(wv + d0) = vout[i];
+    if (!has_v || a.write_v) *reinterpret_cast<vec8*>(wv + d0) = vout[i];
   }
 
   // Rotate the first 2*n_rot dims.
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   // Separate-V layers: windowed ones keep the last W positions in a ring of
   // cache_cap = W slots, global ones every position (slot = position); keys
   // rotated.
-  if (has_v && kc && valid && (a.window == 0 || pos >= a.seq_len - a.window)) {
+  if (v_to_cache) {
     const int slot = a.window > 0 ? pos % a.cache_cap : pos;
     T* dk = kc + (head_base * a.cache_cap + slot) * D;
     T* dv = vc + (head_base * a.cache_cap + slot) * D;

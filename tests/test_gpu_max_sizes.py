@@ -64,3 +64,27 @@ def test_int8_decode_256k_context():
     rows = O.dequantize_rows(cache.codes().cpu().numpy(), cache.scales().cpu().numpy())
     ref = O.decode_from_cache(oracle_layer(shape), to64(q), to64(g_q), rows, None, np.array([CTX_256K]))
     assert_close(out, ref, torch.bfloat16, f"int8 decode at {CTX_256K} cached positions")
+
+
+def test_local_prefill_256k_prompt():
+    """A 256K-position local-layer prompt: one KV head's rows of v span 2^31
+    bytes, so v is staged through the workspace instead of read in place.
+    Early rows (every key they see lies in the first 5K positions) against the
+    oracle, and the ring's last slots."""
+    shape, dev = W.LOCAL_LAYER, device()
+    S = CTX_256K
+    wl = W.with_seq(W.CONFIGS["local_prefill_32k"], S, batch=1)
+    x = wl.draw(dev)
+    lay = api_layer(shape, torch.bfloat16)
+    kc = torch.empty((1, shape.n_kv_heads, shape.window, shape.head_dim), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    out = api.gemma_attn_prefill(lay, x["q"], x["k"], x["v"], x["g_q"], x["g_k"], kc, vc)
+    torch.cuda.synchronize()
+    rows = [0, 1, 1023, 1024, 1025, 4097]
+    hi = max(rows) + 1
+    ref = O.prefill(oracle_layer(shape), to64(x["q"][:, torch.as_tensor(rows, device=dev)]), to64(x["k"][:, :hi]),
+                    to64(x["v"][:, :hi]), to64(x["g_q"]), to64(x["g_k"]), rows=np.asarray(rows), q_at_rows=True)
+    assert_close(out[:, torch.as_tensor(rows, device=dev)], ref, torch.bfloat16, f"local prefill 256K rows {rows}")
+    # the ring holds the last W positions' values unchanged (slot = position mod W)
+    last = torch.arange(S - 8, S, device=dev)
+    assert torch.equal(vc[0, :, last % shape.window].permute(1, 0, 2).cpu(), x["v"][0, last].cpu())
