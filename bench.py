@@ -36,20 +36,20 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 # still match; after any change to them the figure is stale and reads null.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "190403d0781f2189",
-                     "bytes": 15160215846},
-    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "190403d0781f2189",
-                           "bytes": 8590252503},
-    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "190403d0781f2189",
-                           "bytes": 4872737277},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "57caac116dddac0b",
-                      "bytes": 4288873314},
-    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "57caac116dddac0b",
-                            "bytes": 4312480306},
-    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "57caac116dddac0b",
-                                 "bytes": 5355076166},
-    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "57caac116dddac0b",
-                           "bytes": 2173295884},
+    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
+                     "bytes": 23564502361},
+    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
+                           "bytes": 8595434694},
+    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
+                           "bytes": 5867519553},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
+                      "bytes": 4288884005},
+    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
+                            "bytes": 4312488923},
+    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
+                                 "bytes": 5355098353},
+    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
+                           "bytes": 2173300842},
 }
 
 
