@@ -49,7 +49,14 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   constexpr int kMine = kChunks / 8;         // chunks per thread
   typedef T vec8 __attribute__((ext_vector_type(8)));
 
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Workgroup order: the KV heads of every sequence for one tile of positions
+  // run together, so the tile's rows of the cos/sin table are read once into
+  // L2 and then hit there, instead of once per head and sequence.
+  const int n_tiles = a.seq_pad / kPrepTile;
+  const int n_seq = static_cast<int>(gridDim.x) / (a.n_kv_heads * n_tiles);
+  const int h = static_cast<int>(blockIdx.x) % a.n_kv_heads;
+  const int b = (static_cast<int>(blockIdx.x) / a.n_kv_heads) % n_seq;
+  const int tile = static_cast<int>(blockIdx.x) / (a.n_kv_heads * n_seq);
   const int t = threadIdx.x;
   const int r = t >> 3, c8 = t & 7;
   const int pos = tile * kPrepTile + r;
@@ -302,7 +309,7 @@ hipError_t launch_rope_table(void* table, int n_pos, int n_rot, int head_dim, do
 }
 
 hipError_t launch_prefill_prep(const PrepArgs& a, int dtype, int head_dim, int batch, hipStream_t s) {
-  const dim3 grid(a.seq_pad / kPrepTile, a.n_kv_heads, batch);
+  const dim3 grid(static_cast<unsigned>(a.seq_pad / kPrepTile) * a.n_kv_heads * batch);
   if (dtype == 0 && head_dim == 512) hipLaunchKernelGGL((prefill_prep_kernel<bf16, 512>), grid, dim3(256), 0, s, a);
   else if (dtype == 0 && head_dim == 256) hipLaunchKernelGGL((prefill_prep_kernel<bf16, 256>), grid, dim3(256), 0, s, a);
   else if (dtype == 1 && head_dim == 512) hipLaunchKernelGGL((prefill_prep_kernel<float, 512>), grid, dim3(256), 0, s, a);
