@@ -37,19 +37,19 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
-                     "bytes": 23564502361},
+                     "bytes": 23620917664},
     "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
-                           "bytes": 8595434694},
+                           "bytes": 8595479355},
     "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
-                           "bytes": 5867519553},
+                           "bytes": 5852081981},
     "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                      "bytes": 4288884005},
+                      "bytes": 4288878601},
     "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                            "bytes": 4312488923},
+                            "bytes": 4312484700},
     "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                                 "bytes": 5355098353},
+                                 "bytes": 5355097105},
     "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                           "bytes": 2173300842},
+                           "bytes": 2173298130},
 }
 
 
