@@ -240,3 +240,29 @@ def test_int8_global_decode_full_size_sampled():
         rows = oracle_rows(cache.codes()[b:b + 1, :, :L], cache.scales()[b:b + 1, :, :L])
         ref = O.decode_from_cache(ol, to64(q[b:b + 1]), to64(g_q), rows, None, np.array([L]))
         assert_close(out[b:b + 1], ref, torch.bfloat16, f"int8 global decode B16 b={b} L={L}")
+
+
+def test_int8_edge_cases():
+    """Out-of-range append positions write neither codes nor scales; invalid
+    decode lengths give NaN rows next to valid ones."""
+    shape, dev = W.GLOBAL_LAYER, device()
+    D, cap = shape.head_dim, 50
+    lay = q8_layer(shape)
+    cache = api.new_cache(lay, 3, cap, dev)
+    kn = W.normal((3, shape.n_kv_heads, D), 2, "k_new", torch.bfloat16, dev)
+    g = torch.ones(D, dtype=torch.bfloat16, device=dev)
+    api.kv_append(lay, kn, None, g, torch.tensor([-1, cap, cap - 1], dtype=torch.int32, device=dev), cache)
+    torch.cuda.synchronize()
+    c, s = cache.codes().cpu(), cache.scales().cpu()
+    assert not c[:2].any() and not s[:2].any() and not c[2, :, :cap - 1].any() and not s[2, :, :cap - 1].any()
+    assert_codes_match(c[2, :, cap - 1].numpy(), s[2, :, cap - 1].numpy(), O.qk_norm(to64(kn[2]), np.ones(D), 1e-6),
+                       "appended int8 row")
+    codes, scales = W.int8_rows((3, shape.n_kv_heads, 100, D), 3)
+    full = cache_from(lay, codes.to(dev), scales.to(dev))
+    q = W.normal((3, shape.n_q_heads, D), 3, "q_dec", torch.bfloat16, "cpu")
+    bad = torch.tensor([0, 40, 101], dtype=torch.int32, device=dev)   # 0 and 101 are out of range
+    out = api.gemma_attn_decode(lay, q.to(dev), g, full, None, bad, 100).float().cpu()
+    assert torch.isnan(out[0]).all() and torch.isnan(out[2]).all()
+    ref = O.decode_from_cache(oracle_layer(shape), to64(q), np.ones(D), oracle_rows(codes, scales), None,
+                              np.array([0, 40, 100]), batches=[1])
+    assert_close(out[1:2], ref, torch.bfloat16, "int8: valid row next to invalid ones")

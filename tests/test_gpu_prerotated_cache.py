@@ -152,3 +152,32 @@ def test_prerotated_global_decode_full_size_sampled():
         ref = O.decode_from_prerotated_cache(ol, to64(q[b:b + 1]), to64(g_q), to64(cache.heads()[b:b + 1, :, :L]),
                                              to64(cache.rows()[b:b + 1, :, :L]), np.array([L]))
         assert_close(out[b:b + 1], ref, torch.bfloat16, f"pre-rotated global decode B16 b={b} L={L}")
+
+
+def test_prerotated_edge_cases():
+    """Out-of-range append positions write neither rows nor heads; invalid
+    decode lengths give NaN rows next to valid ones."""
+    shape, dev = W.GLOBAL_LAYER, device()
+    D, cap = shape.head_dim, 50
+    lay = pre_layer(shape)
+    cache = api.new_cache(lay, 3, cap, dev)
+    kn = W.normal((3, shape.n_kv_heads, D), 2, "k_new", torch.bfloat16, dev)
+    g = torch.ones(D, dtype=torch.bfloat16, device=dev)
+    api.kv_append(lay, kn, None, g, torch.tensor([-1, cap, cap - 1], dtype=torch.int32, device=dev), cache)
+    torch.cuda.synchronize()
+    r, h = cache.rows().float().cpu(), cache.heads().float().cpu()
+    assert not r[:2].any() and not h[:2].any() and not r[2, :, :cap - 1].any() and not h[2, :, :cap - 1].any()
+    k_hat = O.qk_norm(to64(kn[2]), np.ones(D), 1e-6)
+    assert_close(cache.rows()[2, :, cap - 1], k_hat, torch.bfloat16, "appended row")
+    assert_close(cache.heads()[2, :, cap - 1], O.prerotated_heads(oracle_layer(shape), k_hat[:, None], [cap - 1])[:, 0],
+                 torch.bfloat16, "appended head")
+    lens = [0, 40, 100]
+    lay, full = filled_cache(shape, [100] * 3, seed=5)
+    q = W.normal((3, shape.n_q_heads, D), 5, "q_dec", torch.bfloat16, "cpu")
+    bad = torch.tensor([0, 40, 101], dtype=torch.int32, device=dev)   # 0 and 101 are out of range
+    out = api.gemma_attn_decode(lay, q.to(dev), g, full, None, bad, 100)
+    o = out.float().cpu()
+    assert torch.isnan(o[0]).all() and torch.isnan(o[2]).all()
+    ref = O.decode_from_prerotated_cache(oracle_layer(shape), to64(q), np.ones(D), to64(full.heads()),
+                                         to64(full.rows()), np.array(lens), batches=[1])
+    assert_close(out[1:2], ref, torch.bfloat16, "pre-rotated: valid row next to invalid ones")
