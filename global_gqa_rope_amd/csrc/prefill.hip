@@ -565,11 +565,33 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     kvh = (lin / n_qb) % a.n_kv_heads;
     b = lin / (n_qb * a.n_kv_heads);
   } else {
-    // Causal layers: longest rows first; the round-robin dispatch spreads
-    // every length over all XCDs.
-    qb = n_qb - 1 - static_cast<int>(blockIdx.x);
-    kvh = blockIdx.y;
-    b = blockIdx.z;
+    // Causal layers: longest rows first, and each (sequence, KV head) on a
+    // fixed set of XCDs (a head per XCD and several in turn, or one head over
+    // 8 / H XCDs taking its query blocks in turn), so the workgroups an XCD
+    // runs together stream the same head's key/value tiles through its L2.
+    // Shapes where that is no bijection keep the plain longest-first order.
+    const int H = a.n_kv_heads * static_cast<int>(gridDim.z);
+    const int w = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int x = w % kXcds, i = w / kXcds;
+    int hh = -1, rank = 0;   // (sequence, KV head) and query block rank from the longest
+    if (H % kXcds == 0) {
+      const int hp = H / kXcds;
+      hh = x + kXcds * (i % hp);
+      rank = i / hp;
+    } else if (kXcds % H == 0 && n_qb % (kXcds / H) == 0) {
+      const int k = kXcds / H;
+      hh = x % H;
+      rank = i * k + x / H;
+    }
+    if (hh >= 0) {
+      qb = n_qb - 1 - rank;
+      kvh = hh % a.n_kv_heads;
+      b = hh / a.n_kv_heads;
+    } else {
+      qb = n_qb - 1 - static_cast<int>(blockIdx.x);
+      kvh = blockIdx.y;
+      b = blockIdx.z;
+    }
   }
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
