@@ -36,20 +36,20 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 # still match; after any change to them the figure is stale and reads null.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
-                     "bytes": 23620917664},
-    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
-                           "bytes": 8595479355},
-    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "b7458d8914c8a0f9",
-                           "bytes": 5852081981},
+    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
+                     "bytes": 7829714368},
+    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
+                           "bytes": 8595489218},
+    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
+                           "bytes": 1571526585},
     "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                      "bytes": 4288878601},
+                      "bytes": 4288887639},
     "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                            "bytes": 4312484700},
+                            "bytes": 4312487277},
     "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                                 "bytes": 5355097105},
+                                 "bytes": 5355103654},
     "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                           "bytes": 2173298130},
+                           "bytes": 2173304104},
 }
 
 
