@@ -769,11 +769,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     __syncthreads();
   }
   const float inv = 1.0f / red[0];
+  // Every slot below `count` lies in the partials buffer, so its load needs no
+  // guard and several can be in flight; a zero weight (a share that wrote
+  // nothing, whose slot may hold anything) selects 0 instead of the product.
   for (int d = t; d < D; d += 256) {
-    float o = 0.f;
-    for (int i = 0; i < count; ++i)
-      if (wgt[i] != 0.f) o += wgt[i] * slot(i)[h * D + d];
-    out[d] = from_f32<T>(o * inv);
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    int i = 0;
+    for (; i + 4 <= count; i += 4) {
+      const float v0 = slot(i)[h * D + d], v1 = slot(i + 1)[h * D + d];
+      const float v2 = slot(i + 2)[h * D + d], v3 = slot(i + 3)[h * D + d];
+      o0 += wgt[i] != 0.f ? wgt[i] * v0 : 0.f;
+      o1 += wgt[i + 1] != 0.f ? wgt[i + 1] * v1 : 0.f;
+      o2 += wgt[i + 2] != 0.f ? wgt[i + 2] * v2 : 0.f;
+      o3 += wgt[i + 3] != 0.f ? wgt[i + 3] * v3 : 0.f;
+    }
+    for (; i < count; ++i) {
+      const float v = slot(i)[h * D + d];
+      o0 += wgt[i] != 0.f ? wgt[i] * v : 0.f;
+    }
+    out[d] = from_f32<T>(((o0 + o1) + (o2 + o3)) * inv);
   }
 }
 
