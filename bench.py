@@ -37,19 +37,19 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                     "bytes": 7829714368},
+                     "bytes": 7828029251},
     "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                           "bytes": 8595489218},
+                           "bytes": 8595606057},
     "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                           "bytes": 1571526585},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                      "bytes": 4288887639},
-    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                            "bytes": 4312487277},
-    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                                 "bytes": 5355103654},
-    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d5e7847d75bd08cb",
-                           "bytes": 2173304104},
+                           "bytes": 1572140601},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "163b99fdd4790efc",
+                      "bytes": 4288876933},
+    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "163b99fdd4790efc",
+                            "bytes": 4312483529},
+    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "163b99fdd4790efc",
+                                 "bytes": 5355084081},
+    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "163b99fdd4790efc",
+                           "bytes": 2173315109},
 }
 
 
