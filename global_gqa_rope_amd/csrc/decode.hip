@@ -65,7 +65,11 @@ struct DecodeCfg {
   static constexpr int kDBlocks = D / 16;             // PV output blocks of 16 dims
   static constexpr int kFragBytes = 64 * 8 * kSz;     // one query operand fragment
   static constexpr int kQBytes = kQSteps * kFragBytes;
-  static constexpr int kFineBytes = 16 * kRot * 8;    // cos/sin(j w_i), j < 16, i < kRot
+  // cos/sin(j w_i), j < 16, i < kRot: row j (one key offset) padded by 16 B, so
+  // the 16 rows one rotated QK^T step reads start 4 banks apart instead of all
+  // in the same 4 banks (a 16-way conflict without the pad).
+  static constexpr int kFineRow = kRot > 0 ? kRot * 8 + 16 : 0;
+  static constexpr int kFineBytes = 16 * kFineRow;
   static constexpr int kCoarseBytes = kRot * 8;       // per wave: cos/sin(key0 w_i)
   static constexpr int kPerWaveBytes = kBufs * kTileBytes + 2 * kStageBytes + kCoarseBytes;
   static constexpr int kMiscBytes = 64;               // partition scratch
@@ -491,7 +495,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
     for (int i = threadIdx.x; i < 16 * C::kRot; i += kThreads) {
       float sn, cs;
       sincosf(static_cast<float>((i / C::kRot) * w_pair[0]), &sn, &cs);
-      lds_st<f32x2>(smem0 + C::kFineOff + i * 8, f32x2{cs, sn});
+      lds_st<f32x2>(smem0 + C::kFineOff + (i / C::kRot) * C::kFineRow + (i % C::kRot) * 8, f32x2{cs, sn});
     }
     float sn, cs;
     sincosf(static_cast<float>(C::kWaves * C::KT * w_pair[0]), &sn, &cs);
@@ -502,7 +506,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
   const uint32_t k_lane = key_lane_base<C, T>(tiles, lane);
   const uint32_t v_off = value_lane_base<C, T>(SHARED ? 0 : C::kKBytes, lane);   // within a buffer
   const uint32_t q_lane = smem0 + C::kQOff + lane * 8 * C::kSz;
-  const uint32_t fine_lane = smem0 + C::kFineOff + (hcol * C::kRot + 4 * kg) * 8;
+  const uint32_t fine_lane = smem0 + C::kFineOff + hcol * C::kFineRow + 4 * kg * 8;
   const uint32_t coarse_lane = coarse_s + 4 * kg * 8;
   constexpr float kTau = 8.0f;
   constexpr int kQAhead = 2;   // QK^T steps whose LDS reads are in flight
