@@ -37,19 +37,19 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                     "bytes": 7828029251},
+                     "bytes": 7832416722},
     "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                           "bytes": 8595606057},
+                           "bytes": 8595623934},
     "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                           "bytes": 1572140601},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "163b99fdd4790efc",
-                      "bytes": 4288876933},
-    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "163b99fdd4790efc",
-                            "bytes": 4312483529},
-    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "163b99fdd4790efc",
-                                 "bytes": 5355084081},
-    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "163b99fdd4790efc",
-                           "bytes": 2173315109},
+                           "bytes": 1571469398},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "e0edc6421c32f681",
+                      "bytes": 4288872420},
+    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "e0edc6421c32f681",
+                            "bytes": 4312479311},
+    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "e0edc6421c32f681",
+                                 "bytes": 5355081478},
+    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "e0edc6421c32f681",
+                           "bytes": 2173348765},
 }
 
 
