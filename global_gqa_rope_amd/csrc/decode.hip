@@ -24,7 +24,7 @@
 // All LDS addressing inside the loop is one XOR per read: tiles sit at
 // multiples of their size and rows at multiples of the row size, and a
 // fragment's 16-byte chunk index splits into a lane part and a per-step part
-// with disjoint bits, so the row swizzle (chunk c of row r at c ^ (r & 15))
+// with disjoint bits, so the row swizzle (chunk c of row r at c ^ row_swz(r))
 // turns into lane_base ^ (step part << 4).
 #include <type_traits>
 
@@ -133,9 +133,18 @@ __device__ __forceinline__ int decode_keys(const DecodeArgs& a, int b) {
 }
 
 // Key rows sit in LDS in natural order [key][d]; 16-byte chunk c of row r is
-// stored at chunk c ^ (r & 15), so the 16 rows one QK^T operand read touches
-// fall in distinct banks.
-__device__ __forceinline__ int row_chunk(int r, int c) { return c ^ (r & 15); }
+// stored at chunk c ^ row_swz(r).  Rows are a multiple of 512 B apart, so
+// without the swizzle every row starts in the same bank.  Measured on this
+// chip with SQ_LDS_BANK_CONFLICT: a ds_read_b128 resolves banks over 8
+// consecutive lanes within 128 B, and a ds_read_b64_tr_b16 over 32 lanes
+// within 256 B.  The QK^T key read puts rows 0..7 (or 8..15) on 8 consecutive
+// lanes, one chunk each, so row_swz(r) & 7 must differ across them.  The PV
+// transposing read puts rows 0..7 (or 8..15) on 32 lanes, each row a 32-byte
+// run of chunks 2t, 2t + 1, so row_swz(r) >> 1 must differ across them.
+// row_swz(r) = (r & 7) + 8 (r & 1) satisfies both (c ^ r met only the first:
+// 2-way conflicts on every PV read).
+__device__ __forceinline__ int row_swz(int r) { return (r & 7) | ((r & 1) << 3); }
+__device__ __forceinline__ int row_chunk(int r, int c) { return c ^ row_swz(r); }
 
 // Copy one tile (16 key rows, plus 16 value rows for separate-V layers) from
 // the cache straight into LDS at `dst`.  Each instruction moves 1 KiB: lane l
@@ -242,7 +251,7 @@ __device__ __forceinline__ void value_frag(Frag4<float>& f, const lds_char* buf,
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 4 * (lane >> 4) + j;
-    const uint32_t at = vtile + r * C::kRowBytes + ((cvar ^ r) << 4) + 4 * (lane & 3);
+    const uint32_t at = vtile + r * C::kRowBytes + (row_chunk(r, cvar) << 4) + 4 * (lane & 3);
     f.v[j] = lds_ld<float>(at ^ ((4 * t) << 4));
   }
 }
@@ -252,14 +261,14 @@ template <typename C, typename T>
 __device__ __forceinline__ uint32_t key_lane_base(uint32_t tile, int lane) {
   const int hcol = lane & 15, kg = lane >> 4;
   const int cvar = kg * C::kSz / 2;               // lane part of chunk (32u + 8kg) * size / 16
-  return tile + hcol * C::kRowBytes + ((cvar ^ hcol) << 4);
+  return tile + hcol * C::kRowBytes + (row_chunk(hcol, cvar) << 4);
 }
 template <typename C, typename T>
 __device__ __forceinline__ uint32_t value_lane_base(uint32_t vtile, int lane) {
   if constexpr (std::is_same<T, bf16>::value) {
     const int r = 4 * (lane >> 4) + ((lane & 15) >> 2);
     const int cvar = (lane & 3) >> 1;
-    return vtile + r * C::kRowBytes + ((cvar ^ r) << 4) + 8 * (lane & 1);
+    return vtile + r * C::kRowBytes + (row_chunk(r, cvar) << 4) + 8 * (lane & 1);
   } else {
     return vtile;                                 // the fp32 reads form their own lane addresses
   }
