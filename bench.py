@@ -37,19 +37,19 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                     "bytes": 7832416722},
+                     "bytes": 7829884936},
     "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                           "bytes": 8595623934},
+                           "bytes": 8595751022},
     "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                           "bytes": 1571469398},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "e0edc6421c32f681",
-                      "bytes": 4288872420},
-    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "e0edc6421c32f681",
-                            "bytes": 4312479311},
-    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "e0edc6421c32f681",
-                                 "bytes": 5355081478},
-    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "e0edc6421c32f681",
-                           "bytes": 2173348765},
+                           "bytes": 1570822828},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "ddb3242cba379522",
+                      "bytes": 4288878449},
+    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "ddb3242cba379522",
+                            "bytes": 4312480994},
+    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "ddb3242cba379522",
+                                 "bytes": 5355113227},
+    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "ddb3242cba379522",
+                           "bytes": 2173367760},
 }
 
 
