@@ -176,15 +176,28 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def _on_stream(t: torch.Tensor, stream) -> torch.Tensor:
+    """Mark a tensor this binding allocated as used by `stream` (when one is given).
+
+    Allocations come from the current stream's pool.  A kernel enqueued on
+    another stream may still use the block after the binding returns and drops
+    its reference; record_stream keeps the caching allocator from handing the
+    block out again until that stream's work has finished.
+    """
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
 def gemma_attn_prefill(layer: Layer, q, k, v, q_gain, k_gain, k_cache=None, v_cache=None,
                        out=None, ws=None, stream=None) -> torch.Tensor:
     B, S, Hq, d = q.shape
     Hkv = layer.n_kv_heads
     if out is None:
-        out = torch.empty_like(q)
+        out = _on_stream(torch.empty_like(q), stream)
     need = gemma_attn_prefill_workspace_size(layer, B, S)
     if ws is None:
-        ws = workspace(need, q.device)
+        ws = _on_stream(workspace(need, q.device), stream)
     kc, cap = _cache(layer, k_cache, "k_cache", B)
     vc, vcap = _cache(layer, v_cache, "v_cache", B)
     if v_cache is not None and vcap != cap:
@@ -212,9 +225,9 @@ def gemma_attn_prefill_chunk(layer: Layer, start: int, q, k, q_gain, k_gain, k_c
     Hkv = layer.n_kv_heads
     kc, cap = _cache(layer, k_cache, "k_cache", B)
     if out is None:
-        out = torch.empty_like(q)
+        out = _on_stream(torch.empty_like(q), stream)
     if ws is None:
-        ws = workspace(gemma_attn_prefill_chunk_workspace_size(layer, B, start, T), q.device)
+        ws = _on_stream(workspace(gemma_attn_prefill_chunk_workspace_size(layer, B, start, T), q.device), stream)
     st = _lib.load().gemma_attn_prefill_chunk(
         ctypes.byref(layer.struct()), B, int(start), T, _ptr(q, "q", layer, (B, T, Hq, d)),
         _ptr(k, "k", layer, (B, T, Hkv, d)), _ptr(q_gain, "q_gain", layer, (d,)),
@@ -244,9 +257,9 @@ def gemma_attn_decode(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens, max_s
     kc, cap = _cache(layer, k_cache, "k_cache", B)
     vc, _ = _cache(layer, v_cache, "v_cache", B)
     if out is None:
-        out = torch.empty_like(q)
+        out = _on_stream(torch.empty_like(q), stream)
     if ws is None:
-        ws = workspace(gemma_attn_decode_workspace_size(layer, B, max_seq_len), q.device)
+        ws = _on_stream(workspace(gemma_attn_decode_workspace_size(layer, B, max_seq_len), q.device), stream)
     st = _lib.load().gemma_attn_decode(
         ctypes.byref(layer.struct()), B, _ptr(q, "q", layer, (B, Hq, d)),
         _ptr(q_gain, "q_gain", layer, (d,)), kc, vc, cap,
@@ -269,9 +282,10 @@ def gemma_attn_decode_multi(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens,
     kc, cap = _cache(layer, k_cache, "k_cache", B)
     vc, _ = _cache(layer, v_cache, "v_cache", B)
     if out is None:
-        out = torch.empty_like(q)
+        out = _on_stream(torch.empty_like(q), stream)
     if ws is None:
-        ws = workspace(gemma_attn_decode_multi_workspace_size(layer, B, T, max_seq_len), q.device)
+        ws = _on_stream(workspace(gemma_attn_decode_multi_workspace_size(layer, B, T, max_seq_len), q.device),
+                        stream)
     st = _lib.load().gemma_attn_decode_multi(
         ctypes.byref(layer.struct()), B, T, _ptr(q, "q", layer, (B, T, Hq, d)),
         _ptr(q_gain, "q_gain", layer, (d,)), kc, vc, cap,

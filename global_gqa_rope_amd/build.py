@@ -23,10 +23,13 @@ LIB_NAME = "libgemma_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "prep.hip", "prefill.hip", "decode.hip"]
 ARCH = "gfx950"
-# Per-source device flags.  The decode kernel keeps its 128 fp32 output
-# accumulators in VGPRs and rescales them with VALU ops: MFMAs in VGPR form
-# avoid copying them between the two register files every tile.
-SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source device flags.  MFMAs in VGPR form: the decode kernel keeps its
+# 128 fp32 output accumulators in VGPRs and rescales them with VALU ops; the
+# prefill kernel keeps its QK^T scores in VGPRs, and its output accumulators
+# in AGPRs through MFMAs written out with AGPR operands.  Either way nothing is
+# copied between the two register files every tile.
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -491,24 +491,22 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
   // The lane's rotated QK^T fragments hold key (key0 + hcol) at pairs
   // i = 16u + 4kg + p (u < kRotSteps, p < 4).  cos/sin((key0 + hcol) w_i) =
   // coarse(key0 w_i) (x) fine(hcol w_i): fine is a table shared by the
-  // workgroup; coarse is kept per pair (lane = pair), stepped by the wave's
-  // tile stride (kWaves * 16 positions) each tile and published to the wave
-  // through LDS.  Only the coarse start angle is large (up to the context
-  // length in radians) and needs fp64 sine and cosine; fine and step angles are
-  // below 64 rad, where fp32 sincosf of the fp32-rounded angle is accurate to a
-  // few 1e-6.
+  // workgroup; coarse is kept per pair (lane = pair) and published to the wave
+  // through LDS.  Every factor comes from an fp64 angle with fp64 sine and
+  // cosine, rounded to fp32 once.  Between two tiles of the wave the coarse
+  // factor is stepped by the rotation of the wave's tile stride (kWaves * 16
+  // positions), a complex product that adds a few fp32 roundings per step; so
+  // that those never add up over a long segment, every kAnchor-th tile takes
+  // its coarse factor straight from the fp64 angle again.
+  constexpr int kAnchor = 8;
   f32x2 coarse_l{}, step_l{};
   const uint32_t coarse_s = smem0 + C::kCoarseOff + wave * C::kCoarseBytes;
   if constexpr (C::kRot > 0) {
     static_assert(kThreads % 64 == 0 && C::kRot == 64, "fine table: thread t fills pair t % 64");
-    for (int i = threadIdx.x; i < 16 * C::kRot; i += kThreads) {
-      float sn, cs;
-      sincosf(static_cast<float>((i / C::kRot) * w_pair[0]), &sn, &cs);
-      lds_st<f32x2>(smem0 + C::kFineOff + (i / C::kRot) * C::kFineRow + (i % C::kRot) * 8, f32x2{cs, sn});
-    }
-    float sn, cs;
-    sincosf(static_cast<float>(C::kWaves * C::KT * w_pair[0]), &sn, &cs);
-    step_l = f32x2{cs, sn};
+    for (int i = threadIdx.x; i < 16 * C::kRot; i += kThreads)
+      lds_st<f32x2>(smem0 + C::kFineOff + (i / C::kRot) * C::kFineRow + (i % C::kRot) * 8,
+                    rope_cos_sin(static_cast<double>(i / C::kRot) * w_pair[0]));
+    step_l = rope_cos_sin(static_cast<double>(C::kWaves * C::KT) * w_pair[0]);
   }
 
   const int hcol = lane & 15, kg = lane >> 4;
@@ -645,9 +643,13 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
           s *= row_scale;
         }
         if constexpr (C::kRot > 0) {   // publish the wave's next tile's coarse angles
-          const f32x2 c = coarse_l;
-          coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
-          coarse_l[1] = c[1] * step_l[0] + c[0] * step_l[1];
+          if ((k + 1) % kAnchor == 0) {
+            coarse_l = rope_cos_sin(static_cast<double>(key0 + C::kWaves * C::KT) * w_pair[0]);
+          } else {
+            const f32x2 c = coarse_l;
+            coarse_l[0] = c[0] * step_l[0] - c[1] * step_l[1];
+            coarse_l[1] = c[1] * step_l[0] + c[0] * step_l[1];
+          }
           lds_st<f32x2>(coarse_s + lane * 8, coarse_l);   // read next tile, after the fence below
         }
 

@@ -16,7 +16,9 @@
 //                                the value rows, P straight from the score
 //                                registers
 // Each wave keeps 32 rows x d fp32 accumulators (256 registers at d = 512, in
-// the accumulation register file).
+// the accumulation register file, AGPRs); the scores of a tile stay in VGPRs
+// (MFMAs in VGPR form for QK^T, the PV MFMAs written out with AGPR
+// accumulators).
 //
 // With three or more stages (every bf16 layer) the tile loop is software
 // pipelined: step i takes the row max of tile i's scores, then runs the QK^T
@@ -140,6 +142,24 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<bf16>(lo))) |
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, from_f32<bf16>(hi))) << 16);
+}
+// O += A B for an output block held in the accumulation registers (AGPRs).
+// This file is built with MFMAs in VGPR form, so the QK^T scores stay in
+// VGPRs and all 256 AGPRs hold the 32 x 512 output block of a wave (with the
+// scores' 16 registers also in AGPRs, one output block would not fit and the
+// compiler moved it between the two register files twice per tile: 64 moves
+// per step).  This MFMA is written out so that its accumulator stays in AGPRs.
+// The compiler adds no wait states around it: the s_nop gives the two a
+// VALU write of A or B needs before an MFMA reads it (here the softmax
+// weights, converted by VALU ops); readers of the accumulator wait on their
+// own (update_max, the epilogue).
+__device__ __forceinline__ void mma32_acc(f32x16& c, const Frag8<bf16>& a, const Frag8<bf16>& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a.v), "v"(b.v));
+}
+__device__ __forceinline__ void mma32_acc(f32x16& c, const Frag8<float>& a, const Frag8<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x2_f32 %0, %1, %2, %0" : "+a"(c) : "v"(a.v[j]), "v"(b.v[j]));
 }
 __device__ __forceinline__ float read_acc(float a) {
   float v;
@@ -404,8 +424,12 @@ __device__ __forceinline__ float update_max(const float (&sv)[16], RowState<NB>&
     const float m_new = fmaxf(rs.m_run, mt);
     if (rs.m_run != -INFINITY) {   // nothing accumulated yet otherwise
       const float alpha = __builtin_amdgcn_exp2f(rs.m_run - m_new);
+      // the last output MFMA has retired before its accumulators are read,
+      // and the writes land before the next one reads them
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
       for (int t = 0; t < NB; ++t) scale_acc(rs.o[t], alpha);
+      asm volatile("s_nop 4" ::: "memory");
       rs.l_part *= alpha;
     }
     rs.m_run = m_new;
@@ -439,15 +463,14 @@ __device__ __forceinline__ void pv_tile(const lds_char* st, const LaneOffsets& l
       const Frag8<T> v = vf[f % C::kVAhead];
       if (f + C::kVAhead < 2 * C::kDBlocks)
         value_frag<C>(vf[f % C::kVAhead], st + C::kKBytes, lo.vt, (f + C::kVAhead) >> 1, (f + C::kVAhead) & 1);
-      mma32(rs.o[f >> 1], v, pf[f & 1]);
+      mma32_acc(rs.o[f >> 1], v, pf[f & 1]);
     }
-    interleave_reads_mfma<C::kVAhead, 2 * C::kDBlocks, 2>();
   } else {
 #pragma unroll
     for (int f = 0; f < 2 * C::kDBlocks; ++f) {
       Frag8<T> vf;
       value_frag_f32<C>(vf, st, f >> 1, f & 1, lane);
-      mma32(rs.o[f >> 1], vf, pf[f & 1]);
+      mma32_acc(rs.o[f >> 1], vf, pf[f & 1]);
     }
   }
 }

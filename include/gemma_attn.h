@@ -154,7 +154,15 @@ ga_status gemma_attn_prefill(const ga_layer* layer, int32_t batch, int32_t seq_l
 
 /*
  * Append one new token per sequence to the caches (decode step, before
- * gemma_attn_decode).  The stored form follows the cache conventions above.
+ * gemma_attn_decode).  The cache grows by one position per generated token
+ * as the context lengthens ("Gemma 4 技术报告：开源全模态密集 + MoE 模型家族，长上下文与
+ * 端侧高效是本代核心", section "解决的真问题": the KV cache grows linearly with the
+ * context; "Gemma 4 Technical Report" notes, §2 "Long-context efficiency").
+ * On global K=V layers the row written is the one tensor that later serves as
+ * both key and value ("Gemma 4多模态大模型架构详解", section "K=V"), so one
+ * row per KV head is stored and no v_new is taken; on windowed layers only the
+ * last W positions are kept ("交错层（局部与全局注意力）" of the same page).
+ * The stored form follows the cache conventions above.
  *
  *   k_new   [B, Hkv, d] raw key of the new token;  v_new [B, Hkv, d] raw value
  *           (NULL when kv_shared = 1)
@@ -205,7 +213,17 @@ size_t gemma_attn_decode_workspace_size(const ga_layer* layer, int32_t batch,
                                         int32_t max_seq_len);
 
 /*
- * Decode: one query token per sequence against its cache.  A persistent
+ * Decode: one query token per sequence against its cache.  The query of the
+ * newest position attends to every cached position of a global layer (full
+ * causal) or to the last W of a windowed one ("Gemma 4多模态大模型架构详解",
+ * section "交错层（局部与全局注意力）"), with the G query heads of a group reading
+ * their one KV head (section "分组查询注意力").  On K=V layers the single cached
+ * tensor is read once and used as keys, p-RoPE applied on the fly to its
+ * leading 2 n_rot dims, and, unrotated, as values (section "K=V"; "Gemma 4
+ * Technical Report" notes, §2 "Long-context efficiency", where key = value
+ * on global layers cuts the KV cache).  The cache read grows with the context
+ * ("Gemma 4 技术报告：开源全模态密集 + MoE 模型家族，长上下文与端侧高效是本代核心",
+ * section "解决的真问题"), so this call is bound by HBM bandwidth.  A persistent
  * split-K pass (one workgroup per CU, each streaming an equal share of all
  * cached positions of all sequences and KV heads) is followed by a
  * log-sum-exp merge of the partial results.

@@ -47,6 +47,37 @@ def test_global_decode_256k_context():
         assert_close(out[b:b + 1], ref, torch.bfloat16, f"decode at {L} cached positions")
 
 
+@pytest.mark.parametrize("dtype,q_rot,k_rot", [(torch.bfloat16, 1.0, 1.0), (torch.float32, 4.0, 2.0)],
+                         ids=["bf16", "fp32"])
+def test_global_decode_long_segments_keep_rope_angles(dtype, q_rot, k_rot):
+    """B=32 sequences of 131072 cached positions on a global K=V layer: each of
+    the 256 split-K workgroups streams ~4096 tiles, so a wave runs 1024 (bf16,
+    four waves) or 2048 (fp32, two waves) tiles inside one segment and carries
+    its keys' p-RoPE angles across all of them.  bf16: the workload's N(0, 1)
+    data at the bf16 tolerance.  fp32: the rotated dims (0..127) of q scaled up
+    4x and those of the cache 2x, so that the scores lean on the rotated pairs,
+    at the fp32 tolerance of 1e-5; there an angle error that grows by ~1e-6
+    rad per tile (fp32 rounding of the per-tile rotation step, compounded over
+    2048 tiles) gives, in a float64 simulation, a relative error of 4e-4 and a
+    largest error of 6e-5.  Checked: the first and last sequence."""
+    shape, dev = W.GLOBAL_LAYER, device()
+    B, L, D, Hkv = 32, 131072, shape.head_dim, shape.n_kv_heads
+    lens = torch.full((B,), L, dtype=torch.int32)
+    kc = W.normal((B, Hkv, L, D), 85, "k_cache", dtype, dev)
+    q = W.normal((B, shape.n_q_heads, D), 85, "q_dec", dtype, dev)
+    if q_rot != 1.0:
+        q[..., :128].mul_(q_rot)
+        kc[..., :128].mul_(k_rot)
+    g_q = W.gains(D, 85, "g_q", False, dtype, dev)
+    out = api.gemma_attn_decode(api_layer(shape, dtype), q, g_q, kc, None, lens.to(dev), L)
+    torch.cuda.synchronize()
+    ol = oracle_layer(shape)
+    for b in [0, B - 1]:
+        ref = O.decode_from_cache(ol, to64(q[b:b + 1]), to64(g_q), to64(kc[b:b + 1]), None, np.array([L]))
+        assert_close(out[b:b + 1], ref, dtype, f"decode {dtype} B=32 L={L} b={b} (long segments)")
+    del kc
+
+
 def test_int8_decode_256k_context():
     shape, dev = W.GLOBAL_LAYER, device()
     D = shape.head_dim
