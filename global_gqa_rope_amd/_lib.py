@@ -49,6 +49,7 @@ SIGNATURES = {
     "gemma_attn_decode": (_I, [_LP, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
     "gemma_attn_decode_multi_workspace_size": (_Z, [_LP, _I, _I, _I]),
     "gemma_attn_decode_multi": (_I, [_LP, _I, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _Z, _P]),
+    "gemma_attn_decode_noalloc": (_I, [_LP, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P]),
     "gemma_attn_cache_bytes": (_Z, [_LP, _I, _I]),
     "gemma_attn_last_error": (ctypes.c_char_p, []),
     "gemma_attn_version": (ctypes.c_char_p, []),

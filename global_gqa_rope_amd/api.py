@@ -270,6 +270,22 @@ def gemma_attn_decode(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens, max_s
     return out
 
 
+def gemma_attn_decode_noalloc(layer: Layer, q, q_gain, k_cache, v_cache, seq_lens, max_seq_len: int, out,
+                              stream=None) -> torch.Tensor:
+    """gemma_attn_decode on the library's static per-GPU scratch: neither this
+    binding nor the library allocates device memory, so `out` is required."""
+    B, Hq, d = q.shape
+    kc, cap = _cache(layer, k_cache, "k_cache", B)
+    vc, _ = _cache(layer, v_cache, "v_cache", B)
+    st = _lib.load().gemma_attn_decode_noalloc(
+        ctypes.byref(layer.struct()), B, _ptr(q, "q", layer, (B, Hq, d)),
+        _ptr(q_gain, "q_gain", layer, (d,)), kc, vc, cap,
+        _ptr(seq_lens, "seq_lens", dtype=torch.int32, shape=(B,)), int(max_seq_len),
+        _ptr(out, "out", layer, (B, Hq, d)), _stream(stream))
+    _lib.check(st)
+    return out
+
+
 def gemma_attn_decode_multi_workspace_size(layer: Layer, batch: int, q_len: int, max_seq_len: int) -> int:
     return int(_lib.load().gemma_attn_decode_multi_workspace_size(ctypes.byref(layer.struct()), batch, q_len,
                                                                     max_seq_len))

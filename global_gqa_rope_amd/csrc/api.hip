@@ -238,6 +238,46 @@ ga_status check_workspace(void* ws, size_t have, size_t need) {
   return GA_OK;
 }
 
+// ---- scratch for the decode that allocates nothing ------------------------------
+// One static device array per GPU, reached through its address on that device
+// (hipGetSymbolAddress); the array's name in host code is only a stand-in.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+
+__global__ void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // per device: the scratch array's device address
+
+// The current device's scratch address, found (and the array cleared, by a
+// fill kernel on `s`) on the first call on that device.
+ga_status device_scratch(int dev, hipStream_t s, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0) return fail(GA_EINVAL, "bad device index %d", dev);
+  if (static_cast<size_t>(dev) >= g_scratch_ptr.size()) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "decode scratch: hipGetSymbolAddress");
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(p),
+                       kNoAllocScratchBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "decode scratch: clearing launch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GA_OK;
+}
+
 }  // namespace
 
 // Decode launches two kernels; the launcher reports each to this callback.
@@ -256,6 +296,72 @@ void record_decode(hipStream_t s, int which, bool before) {
   g_prof.push_back({which, pending, stop});
   pending = nullptr;
 }
+
+namespace {
+
+// Decode of the last q_len positions of each sequence.  `noalloc`: the
+// split-K scratch is this device's static scratch array instead of
+// `workspace`, and a plan that needs more than it holds is rejected.
+ga_status decode_impl(const ga_layer* layer, int32_t batch, int32_t q_len, const void* q, const void* q_gain,
+                      const void* k_cache, const void* v_cache, int32_t cache_cap, const int32_t* seq_lens,
+                      int32_t max_seq_len, void* out, void* workspace, size_t workspace_bytes, bool noalloc,
+                      void* stream) {
+  Derived dv;
+  ga_status st = check_layer(layer, &dv);
+  if (st != GA_OK) return st;
+  if (batch < 0) return fail(GA_EINVAL, "batch must be >= 0");
+  st = check_q_len(layer, dv, q_len);
+  if (st != GA_OK) return st;
+  if (batch == 0) return GA_OK;
+  if (max_seq_len < 1) return fail(GA_EINVAL, "max_seq_len must be >= 1");
+  if (static_cast<int64_t>(batch) * layer->n_kv_heads * decode_tiles_per_seq(layer, max_seq_len) > INT32_MAX)
+    return fail(GA_EUNSUPPORTED, "batch %d x max_seq_len %d: too many cached positions for one decode call", batch,
+                max_seq_len);
+  if (!q || !q_gain || !seq_lens || !out) return fail(GA_EINVAL, "q, q_gain, seq_lens and out must be non-NULL");
+  if (layer->dtype == GA_F32 && layer->head_dim == 512 && !layer->kv_shared)
+    return fail(GA_EUNSUPPORTED, "fp32 decode with head_dim 512 and a separate V cache is not built");
+  st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
+  if (st != GA_OK) return st;
+  if (static_cast<int64_t>(cache_cap) * layer->head_dim * (dv.q8 ? 1 : dv.elem) > INT32_MAX)
+    return fail(GA_EUNSUPPORTED, "cache_cap %d: one head's cache must stay under 2 GiB for decode", cache_cap);
+  if (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16)
+    return fail(GA_EINVAL, "the caches must be 16-byte aligned");
+  if (!noalloc) {
+    st = check_workspace(workspace, workspace_bytes, decode_bytes(layer, dv, batch, q_len, max_seq_len));
+    if (st != GA_OK) return st;
+  }
+  int dev = 0, cus = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he == hipSuccess) he = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (he != hipSuccess) return hip_status(he, "decode: device query");
+  ga::DecodePlan plan;
+  if (!decode_plan(layer, dv, batch, q_len, max_seq_len, cus, &plan))
+    return fail(GA_EUNSUPPORTED, "no decode kernel for this layer configuration");
+  if (noalloc) {
+    if (plan.bytes() > kNoAllocScratchBytes)
+      return fail(GA_EWORKSPACE, "decode needs %zu bytes of scratch for batch %d, max_seq_len %d; the static "
+                  "scratch holds %zu (use gemma_attn_decode with a workspace)", plan.bytes(), batch, max_seq_len,
+                  kNoAllocScratchBytes);
+    st = device_scratch(dev, static_cast<hipStream_t>(stream), &workspace);
+    if (st != GA_OK) return st;
+  }
+  ga::DecodeArgs da{};
+  da.q = q; da.q_gain = q_gain; da.k_cache = k_cache; da.v_cache = v_cache; da.seq_lens = seq_lens;
+  da.out = out;
+  da.tile_prefix = static_cast<int32_t*>(workspace);
+  da.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.prefix_bytes);
+  da.batch = batch; da.n_q_heads = layer->n_q_heads; da.n_kv_heads = layer->n_kv_heads; da.n_rot = dv.n_rot;
+  da.window = layer->window; da.cache_cap = cache_cap; da.max_seq_len = max_seq_len; da.n_wgs = plan.n_wgs;
+  da.q_len = q_len; da.slot_floats = static_cast<int>(plan.slot_floats);
+  da.k_scales = q8_scales(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
+  da.k_heads = pre_heads(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
+  da.eps = layer->norm_eps; da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
+  return hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
+                                      static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),
+                    "decode launch");
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -452,50 +558,15 @@ ga_status gemma_attn_decode_multi(const ga_layer* layer, int32_t batch, int32_t 
                                   const void* q_gain, const void* k_cache, const void* v_cache, int32_t cache_cap,
                                   const int32_t* seq_lens, int32_t max_seq_len, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  Derived dv;
-  ga_status st = check_layer(layer, &dv);
-  if (st != GA_OK) return st;
-  if (batch < 0) return fail(GA_EINVAL, "batch must be >= 0");
-  st = check_q_len(layer, dv, q_len);
-  if (st != GA_OK) return st;
-  if (batch == 0) return GA_OK;
-  if (max_seq_len < 1) return fail(GA_EINVAL, "max_seq_len must be >= 1");
-  if (static_cast<int64_t>(batch) * layer->n_kv_heads * decode_tiles_per_seq(layer, max_seq_len) > INT32_MAX)
-    return fail(GA_EUNSUPPORTED, "batch %d x max_seq_len %d: too many cached positions for one decode call", batch,
-                max_seq_len);
-  if (!q || !q_gain || !seq_lens || !out) return fail(GA_EINVAL, "q, q_gain, seq_lens and out must be non-NULL");
-  if (layer->dtype == GA_F32 && layer->head_dim == 512 && !layer->kv_shared)
-    return fail(GA_EUNSUPPORTED, "fp32 decode with head_dim 512 and a separate V cache is not built");
-  st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
-  if (st != GA_OK) return st;
-  if (static_cast<int64_t>(cache_cap) * layer->head_dim * (dv.q8 ? 1 : dv.elem) > INT32_MAX)
-    return fail(GA_EUNSUPPORTED, "cache_cap %d: one head's cache must stay under 2 GiB for decode", cache_cap);
-  if (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16)
-    return fail(GA_EINVAL, "the caches must be 16-byte aligned");
-  const size_t need = decode_bytes(layer, dv, batch, q_len, max_seq_len);
-  st = check_workspace(workspace, workspace_bytes, need);
-  if (st != GA_OK) return st;
-  int dev = 0, cus = 0;
-  hipError_t he = hipGetDevice(&dev);
-  if (he == hipSuccess) he = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (he != hipSuccess) return hip_status(he, "decode: device query");
-  ga::DecodePlan plan;
-  if (!decode_plan(layer, dv, batch, q_len, max_seq_len, cus, &plan))
-    return fail(GA_EUNSUPPORTED, "no decode kernel for this layer configuration");
-  ga::DecodeArgs da{};
-  da.q = q; da.q_gain = q_gain; da.k_cache = k_cache; da.v_cache = v_cache; da.seq_lens = seq_lens;
-  da.out = out;
-  da.tile_prefix = static_cast<int32_t*>(workspace);
-  da.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.prefix_bytes);
-  da.batch = batch; da.n_q_heads = layer->n_q_heads; da.n_kv_heads = layer->n_kv_heads; da.n_rot = dv.n_rot;
-  da.window = layer->window; da.cache_cap = cache_cap; da.max_seq_len = max_seq_len; da.n_wgs = plan.n_wgs;
-  da.q_len = q_len; da.slot_floats = static_cast<int>(plan.slot_floats);
-  da.k_scales = q8_scales(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
-  da.k_heads = pre_heads(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
-  da.eps = layer->norm_eps; da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
-  return hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
-                                      static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),
-                    "decode launch");
+  return decode_impl(layer, batch, q_len, q, q_gain, k_cache, v_cache, cache_cap, seq_lens, max_seq_len, out,
+                     workspace, workspace_bytes, false, stream);
+}
+
+ga_status gemma_attn_decode_noalloc(const ga_layer* layer, int32_t batch, const void* q, const void* q_gain,
+                                    const void* k_cache, const void* v_cache, int32_t cache_cap,
+                                    const int32_t* seq_lens, int32_t max_seq_len, void* out, void* stream) {
+  return decode_impl(layer, batch, 1, q, q_gain, k_cache, v_cache, cache_cap, seq_lens, max_seq_len, out, nullptr, 0,
+                     true, stream);
 }
 
 }  // extern "C"

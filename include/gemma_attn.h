@@ -282,6 +282,31 @@ ga_status gemma_attn_decode_multi(const ga_layer* layer, int32_t batch, int32_t 
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * gemma_attn_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: the split-K scratch (per-sequence tile
+ * offsets and partial results) is a static 32 MiB device array of the
+ * library, one copy per GPU, held until the process ends.  On the first call
+ * on a device the library looks up that copy's address and clears it with a
+ * fill kernel on `stream`.  Nothing is allocated, by this call or the library.
+ *
+ * Arguments, layouts and results are those of gemma_attn_decode (the same
+ * kernels and launch shape; the output matches it bit for bit).
+ * GA_EWORKSPACE if the call would need more than 32 MiB of scratch (about
+ * 4 * (CUs + batch * Hkv) * (G * d + 64) * 4 bytes, e.g. batch 64 with 4 KV
+ * heads of G = 8, d = 512 on 256 CUs needs 32.5 MiB); use gemma_attn_decode
+ * with a workspace then.  Every call on one GPU shares that GPU's array and
+ * finds the previous call's contents there: calls that overlap on one GPU
+ * (several streams, or several threads) race and must be serialised by the
+ * caller.
+ */
+ga_status gemma_attn_decode_noalloc(const ga_layer* layer, int32_t batch,
+                                    const void* q, const void* q_gain,
+                                    const void* k_cache, const void* v_cache,
+                                    int32_t cache_cap, const int32_t* seq_lens,
+                                    int32_t max_seq_len, void* out, void* stream);
+
+/*
  * Measurement hooks (not part of the computation).  While enabled, every
  * launch of the kernels below is bracketed by a pair of HIP events recorded
  * on the caller's stream; gemma_attn_profile_read() waits for the recorded
