@@ -172,10 +172,14 @@ def bench_decode(args, torch, api, W):
     append_ms, n_append = api.profile_read("kv_append")
     api.profile_reset()
     nbytes = wl.kv_bytes(lens)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_decode(wl, lens, kc, q, g_q, args.cpu_seconds / 3, torch)
     del kc
     torch.cuda.empty_cache()
     return {"sec": sec, "bytes": nbytes, "split_ms": split_ms / max(n_split, 1),
-            "merge_ms": merge_ms / max(n_merge, 1), "append_ms": append_ms / max(n_append, 1), "lens": lens}
+            "merge_ms": merge_ms / max(n_merge, 1), "append_ms": append_ms / max(n_append, 1), "lens": lens,
+            "cpu": cpu}
 
 
 def bench_local_prefill(args, torch, api, W):
@@ -476,14 +480,58 @@ def bench_stack_decode(args, torch, api, W):
     }
 
 
+def host_info():
+    """The host the oracle runs on: core counts, CPU model and the BLAS threads numpy uses."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = None
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"nproc": os.cpu_count(), "affinity": affinity, "cpu_model": model, "blas_threads": blas}
+
+
+def cpu_baseline_decode(wl, lens, kc, q, g_q, budget_s, torch):
+    """The oracle's decode on whole sequences of the same B=16 decode workload
+    (every KV head of a sequence, all its cached positions), as GB/s of cache."""
+    import oracle as O
+    shape = wl.layer
+    ol = O.OracleLayer(shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.window, shape.kv_shared,
+                       shape.rope_theta, shape.rope_fraction, shape.norm_eps)
+    g64 = g_q.to("cpu", torch.float64).numpy()
+    order = np.argsort(lens.numpy())          # shortest sequences first, so the budget covers several
+    done, nbytes, elapsed = [], 0, 0.0
+    for b in order:
+        if elapsed >= budget_s:
+            break
+        L = int(lens[b])
+        kb = kc[b:b + 1, :, :L].to("cpu", torch.float64).numpy()
+        qb = q[b:b + 1].to("cpu", torch.float64).numpy()
+        t0 = time.perf_counter()
+        O.decode_from_cache(ol, qb, g64, kb, None, np.array([L]))
+        elapsed += time.perf_counter() - t0
+        done.append(L)
+        nbytes += L * shape.n_kv_heads * shape.head_dim * 2
+    return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "kind": "oracle",
+            "sample": f"{len(done)} whole sequences of the B=16 global decode (lengths {min(done)}..{max(done)}, "
+                      f"all 4 KV heads), float64 numpy, {elapsed:.1f} s timed (the host copy and cast excluded); "
+                      "GB/s counts the bf16 cache bytes the step reads"}
+
+
 def cpu_baseline(pre, budget_s, torch):
     """The oracle as it stands, on a bounded sample of the same prefill."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
+    host = host_info()
+    cores = host["blas_threads"] or host["nproc"] or 1
     wl, x = pre["wl"], pre["x"]
     shape = wl.layer
     ol = O.OracleLayer(shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.window, shape.kv_shared,
@@ -505,7 +553,8 @@ def cpu_baseline(pre, budget_s, torch):
         elapsed = time.perf_counter() - t0
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{done_rows} random query rows of the same 32K global prefill (all 32 heads), "
-                      f"float64 numpy, {elapsed:.1f} s incl. key norm/rotation per call"}
+                      f"float64 numpy, {elapsed:.1f} s incl. key norm/rotation per call",
+            "host": host}
 
 
 def main():
@@ -525,6 +574,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    cpu_dec = None
     pre = bench_prefill(args, torch, api, W)
     tflops = pre["flops"] / pre["sec"] / 1e12
     attn_tflops = pre["flops"] / (pre["attn_ms"] * 1e-3) / 1e12
@@ -565,6 +615,7 @@ def main():
                          "avg_ms": round(dec["split_ms"], 4), "merge_avg_ms": round(dec["merge_ms"], 4)},
             "kv_append_avg_ms": round(dec["append_ms"], 4),
         }
+        cpu_dec = dec["cpu"]
     if not args.no_multi:
         line["multi_token_decode"] = bench_multi_decode(args, torch, api, W)
     if not args.no_prerotated:
@@ -585,6 +636,8 @@ def main():
         line["stack_decode"] = bench_stack_decode(args, torch, api, W)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds, torch)
+        if not args.no_decode and cpu_dec is not None:
+            line["cpu_baseline"]["decode"] = cpu_dec
     print(json.dumps(line), flush=True)
 
 
