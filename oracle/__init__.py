@@ -43,6 +43,7 @@ from .attention import (  # noqa: F401
     prerotated_heads,
     qk_norm,
     quantize_rows,
+    ring_positions,
     rope_frequencies,
     rotate,
     rotated_pairs,

@@ -202,7 +202,11 @@ def prefill(layer: OracleLayer, q, k, v, g_q, g_k, rows=None,
 # --- Caches ------------------------------------------------------------------
 # Global layers: one tensor serves as keys and values, stored normalised and
 # unrotated; p-RoPE is applied when the scores are formed.  Local layers: a
-# ring of W slots for the normalised, rotated key and the raw value.
+# ring of cache_cap >= W slots (slot = position mod cache_cap) for the
+# normalised, rotated key and the raw value.  W slots hold every key the
+# newest token sees; checking T new tokens at once needs W + T - 1, since the
+# earliest of them still sees T - 1 positions the later ones pushed out of a
+# W-slot ring.
 
 def expected_caches_after_prefill(layer: OracleLayer, k, v, g_k, cache_cap: int):
     """Cache contents [B,Hkv,cap,d] after a prompt of S tokens (unwritten = nan)."""
@@ -215,11 +219,11 @@ def expected_caches_after_prefill(layer: OracleLayer, k, v, g_k, cache_cap: int)
             raise ValueError("prompt longer than the cache")
         kc[:, :, :S] = k_hat.transpose(0, 2, 1, 3)
         return kc, None
-    # Separate V: keys stored rotated.  Windowed layers keep a ring of W
-    # slots (slot = position mod W); global ones every position (slot =
-    # position), as the E2B/E4B global layers without K=V need.
-    if layer.window > 0 and cache_cap != layer.window:
-        raise ValueError("a local cache has exactly W slots")
+    # Separate V: keys stored rotated.  Windowed layers keep a ring of
+    # cache_cap >= W slots (slot = position mod cache_cap); global ones every
+    # position (slot = position), as the E2B/E4B global layers without K=V need.
+    if layer.window > 0 and cache_cap < layer.window:
+        raise ValueError("a local cache has at least W slots")
     if layer.window == 0 and S > cache_cap:
         raise ValueError("prompt longer than the cache")
     positions = np.arange(S)
@@ -249,6 +253,13 @@ def expected_caches_after_append(layer: OracleLayer, k_cache, v_cache, k_new,
     return kc, vc
 
 
+def ring_positions(seq_len: int, cache_cap: int) -> np.ndarray:
+    """Positions held by the min(L, cap) filled slots of a ring after L tokens:
+    slot s holds the latest position congruent to s mod cap."""
+    L = int(seq_len)
+    return np.array([L - 1 - ((L - 1 - s) % cache_cap) for s in range(min(L, cache_cap))], dtype=np.int64)
+
+
 def decode_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
                       batches=None) -> np.ndarray:
     """One decode step per sequence: q [B,Hq,d] raw, query position L_b - 1.
@@ -256,8 +267,8 @@ def decode_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
     ``seq_lens[b]`` counts the valid keys including the new token.  Global
     layers read slots 0..L_b-1 (slot j = position j): K=V caches are rotated on
     the fly, separate-V caches hold rotated keys.  Local layers read the
-    min(L_b, W) filled ring slots, whose keys are stored already rotated.
-    Returns out [len(batches), Hq, d].
+    min(L_b, cap) filled ring slots, whose keys are stored already rotated, and
+    see those inside the window.  Returns out [len(batches), Hq, d].
     """
     G = layer.group
     batches = range(q.shape[0]) if batches is None else batches
@@ -283,10 +294,8 @@ def decode_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_lens,
                 rows[h] = masked_softmax_attention(
                     q_rot[h:h + 1], qpos, k_cache[b, h // G, :L], v_cache[b, h // G, :L], kpos, layer.scale, 0)[0]
         else:
-            n = min(L, layer.window)
-            # Slot s holds the latest position congruent to s mod W; all of the
-            # n filled slots lie inside the window of the query at L - 1.
-            kpos = np.array([L - 1 - ((L - 1 - s) % layer.window) for s in range(n)])
+            kpos = ring_positions(L, k_cache.shape[2])
+            n = kpos.size
             for h in range(layer.n_q_heads):
                 rows[h] = masked_softmax_attention(
                     q_rot[h:h + 1], qpos, k_cache[b, h // G, :n],
@@ -301,15 +310,16 @@ def decode_multi_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_le
 
     q [B,T,Hq,d] raw; token j of sequence b sits at position L_b - T + j, where
     ``seq_lens[b]`` = L_b counts the valid keys including all T new tokens, and
-    attends to cache slots 0 .. its own position (global layers only: slot =
-    position; the K=V cache's unrotated keys are rotated on the fly and used
-    unrotated as values).  This is the check of tokens proposed by the MTP
-    drafter ("Gemma 4 Technical Report" notes, section 2.6): each is attention
-    at its own position, the definition of ``prefill`` row by row.  Returns
-    out [len(batches), T, Hq, d].
+    attends to the cached keys at positions up to its own (and, on windowed
+    layers, above its own minus W).  Global layers: slot = position; a K=V
+    cache's unrotated keys are rotated on the fly and used unrotated as values,
+    a separate-V cache holds rotated keys.  Windowed layers: a ring of cap
+    slots holding rotated keys, which must still hold every key the earliest
+    token sees (cap >= W + T - 1 once the ring has wrapped).  This is the check
+    of tokens proposed by the MTP drafter ("Gemma 4 Technical Report" notes,
+    section 2.6): each is attention at its own position, the definition of
+    ``prefill`` row by row.  Returns out [len(batches), T, Hq, d].
     """
-    if layer.window or not layer.kv_shared:
-        raise ValueError("several new tokens at once are defined here for global K=V layers only")
     G, T = layer.group, q.shape[1]
     batches = range(q.shape[0]) if batches is None else batches
     out = []
@@ -320,13 +330,23 @@ def decode_multi_from_cache(layer: OracleLayer, q, g_q, k_cache, v_cache, seq_le
         qpos = L - T + np.arange(T)
         q_hat = qk_norm(q[b], g_q, layer.norm_eps)                             # [T,Hq,d]
         q_rot = rotate(q_hat, qpos[:, None], layer.rope_theta, layer.rope_fraction)
-        kpos = np.arange(L)
+        if layer.window:
+            kpos = ring_positions(L, k_cache.shape[2])
+            if kpos.min() > max(0, int(qpos[0]) - layer.window + 1):
+                raise ValueError("the ring no longer holds keys the earliest new token sees")
+        else:
+            kpos = np.arange(L)
+        n = kpos.size
         rows = np.empty((T, layer.n_q_heads, layer.head_dim))
         for c in range(layer.n_kv_heads):
-            keys = _f64(k_cache[b, c, :L])
-            k_rot = rotate(keys, kpos, layer.rope_theta, layer.rope_fraction)
+            stored = _f64(k_cache[b, c, :n])
+            if layer.kv_shared:
+                keys, vals = rotate(stored, kpos, layer.rope_theta, layer.rope_fraction), stored
+            else:
+                keys, vals = stored, _f64(v_cache[b, c, :n])
             for h in range(c * G, (c + 1) * G):
-                rows[:, h] = masked_softmax_attention(q_rot[:, h], qpos, k_rot, keys, kpos, layer.scale, 0)
+                rows[:, h] = masked_softmax_attention(q_rot[:, h], qpos, keys, vals, kpos, layer.scale,
+                                                      layer.window)
         out.append(rows)
     return np.stack(out)
 

@@ -313,7 +313,14 @@ def test_softmax_scale_default_is_inverse_sqrt_head_dim():
 
 # --------------------------------------------------- decode and caches ----
 
-@pytest.mark.parametrize("kind", ["global", "global_separate_v", "local"])
+def test_ring_positions_hand_values():
+    # 10 tokens in a 4-slot ring: slots 0..3 hold positions 8, 9, 6, 7
+    assert O.ring_positions(10, 4).tolist() == [8, 9, 6, 7]
+    assert O.ring_positions(3, 4).tolist() == [0, 1, 2]
+    assert O.ring_positions(8, 4).tolist() == [4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("kind", ["global", "global_separate_v", "local", "local_wide_ring"])
 def test_decode_from_cache_equals_prefill_row(kind):
     d = 32
     if kind == "global":
@@ -330,7 +337,8 @@ def test_decode_from_cache_equals_prefill_row(kind):
     g_q = RNG.normal(1, 0.1, size=d)
     g_k = RNG.normal(1, 0.1, size=d)
     full = O.prefill(lay, q, k, v, g_q, g_k)
-    cap = lay.window if lay.window else T
+    # a ring wider than the window keeps older keys, which the window must mask
+    cap = (lay.window + 3 if kind == "local_wide_ring" else lay.window) if lay.window else T
     kc, vc = O.expected_caches_after_prefill(lay, k[:, :T - 4],
                                              None if v is None else v[:, :T - 4], g_k, cap)
     for t in range(T - 4, T):
@@ -341,20 +349,30 @@ def test_decode_from_cache_equals_prefill_row(kind):
         assert np.allclose(got, full[:, t], atol=1e-13)
 
 
-@pytest.mark.parametrize("group", [8, 2])
-def test_multi_token_decode_equals_the_prefill_rows(group):
+@pytest.mark.parametrize("kind,group", [("global", 8), ("global", 2), ("global_separate_v", 4), ("local", 2),
+                                        ("local", 4)])
+def test_multi_token_decode_equals_the_prefill_rows(kind, group):
     """Several new tokens at once: token j is the prefill row at its position,
-    over a cache built by a prefill of the older tokens plus appends."""
+    over a cache built by a prefill of the older tokens plus appends.  The
+    local case uses a ring of W + T - 1 = 8 slots and new tokens at positions
+    7, 8, 9, whose slots (7, 0, 1) wrap inside the new tokens."""
     d = 32
-    lay = layer(hq=2 * group, hkv=2, d=d, kv_shared=True, theta=1e6, p=0.25)
     B, S, T = 2, 13, 3
+    if kind == "global":
+        lay = layer(hq=2 * group, hkv=2, d=d, kv_shared=True, theta=1e6, p=0.25)
+    elif kind == "global_separate_v":
+        lay = layer(hq=2 * group, hkv=2, d=d, kv_shared=False, theta=1e6, p=0.25)
+    else:
+        lay = layer(hq=2 * group, hkv=2, d=d, window=6, theta=1e4, p=1.0)
+        S = 10
+    cap = lay.window + T - 1 if lay.window else S
     q = RNG.normal(size=(B, S, lay.n_q_heads, d))
     k = RNG.normal(size=(B, S, lay.n_kv_heads, d))
-    v = None
+    v = None if lay.kv_shared else RNG.normal(size=(B, S, lay.n_kv_heads, d))
     g_q = RNG.normal(1, 0.1, size=d)
     g_k = RNG.normal(1, 0.1, size=d)
     full = O.prefill(lay, q, k, v, g_q, g_k)
-    kc, vc = O.expected_caches_after_prefill(lay, k[:, :S - T], None if v is None else v[:, :S - T], g_k, S)
+    kc, vc = O.expected_caches_after_prefill(lay, k[:, :S - T], None if v is None else v[:, :S - T], g_k, cap)
     for t in range(S - T, S):
         kc, vc = O.expected_caches_after_append(lay, kc, vc, k[:, t], None if v is None else v[:, t], g_k,
                                                 np.full(B, t))
@@ -378,9 +396,12 @@ def test_multi_token_decode_masks_the_later_new_tokens():
     kc2[0, 0, 5] += 1.0                               # the key of the second new token (position 5)
     b = O.decode_multi_from_cache(lay, q, g, kc2, None, np.array([6]))
     assert np.array_equal(a[:, 0], b[:, 0]) and not np.allclose(a[:, 1], b[:, 1])
-    with pytest.raises(ValueError):      # windowed and separate-V layers are not defined here
-        O.decode_multi_from_cache(layer(hq=2, hkv=1, d=d, window=3, theta=1e4, p=1.0), q, g, kc, kc,
-                                  np.array([6]))
+    # a W-slot ring after 6 tokens holds positions 3..5: the first of two new
+    # tokens (position 4, window 3) needs position 2, which it no longer holds
+    loc = layer(hq=2, hkv=1, d=d, window=3, theta=1e4, p=1.0)
+    with pytest.raises(ValueError):
+        O.decode_multi_from_cache(loc, q, g, kc[:, :, :3], kc[:, :, :3], np.array([6]))
+    O.decode_multi_from_cache(loc, q, g, kc[:, :, :4], kc[:, :, :4], np.array([6]))   # W + 1 slots suffice
 
 
 def test_int8_rows_hand_values_and_bounds():
