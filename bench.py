@@ -80,6 +80,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-local", action="store_true", help="skip the local-layer prefill leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 6-layer stack decode leg")
+    ap.add_argument("--no-verify", action="store_true", help="skip the 6-layer two-token verification leg")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-token decode leg")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8-cache decode leg")
     ap.add_argument("--no-prerotated", action="store_true", help="skip the pre-rotated-cache decode leg")
@@ -527,6 +528,65 @@ def cpu_baseline_decode(wl, lens, kc, q, g_q, budget_s, torch):
                       "GB/s counts the bf16 cache bytes the step reads"}
 
 
+def bench_stack_verify(args, torch, api, W, q_len=2):
+    """One verification step of the 6-layer stack (5 local + 1 global): each
+    layer appends q_len drafted tokens per sequence, then checks them in one
+    gemma_attn_decode_multi call (local rings of W + q_len - 1 slots)."""
+    wl_l, wl_g = W.CONFIGS["stack_decode_local"], W.CONFIGS["stack_decode_global"]
+    dev = torch.device("cuda", 0)
+    B = wl_l.batch
+    layers = []
+    for i, wl in enumerate([wl_l] * 5 + [wl_g]):
+        shape = wl.layer
+        D, Hkv = shape.head_dim, shape.n_kv_heads
+        seed = wl.seed + i
+        cap = shape.window + q_len - 1 if shape.window else wl.ctx_hi + q_len
+        kc = W.normal((B, Hkv, cap, D), seed, "k_cache", torch.bfloat16, dev)
+        vc = None if shape.kv_shared else W.normal((B, Hkv, cap, D), seed, "v_cache", torch.bfloat16, dev)
+        lens = wl.lengths() + (q_len - 1)          # context + q_len new tokens
+        lay = api.Layer.from_shape(shape, torch.bfloat16)
+        n_keys = [min(int(n), cap) if shape.window else int(n) for n in lens]
+        layers.append({
+            "lay": lay, "kc": kc, "vc": vc, "seq": lens.to(dev), "max": int(lens.max()),
+            "pos": [(lens - q_len + j).to(dev) for j in range(q_len)],
+            "q": W.normal((B, q_len, shape.n_q_heads, D), seed, "q_dec", torch.bfloat16, dev),
+            "kn": W.normal((q_len, B, Hkv, D), seed, "k_new", torch.bfloat16, dev),
+            "vn": None if shape.kv_shared else W.normal((q_len, B, Hkv, D), seed, "v_new", torch.bfloat16, dev),
+            "g_q": W.gains(D, seed, "g_q", False, torch.bfloat16, dev),
+            "g_k": W.gains(D, seed, "g_k", False, torch.bfloat16, dev),
+            "out": torch.empty((B, q_len, shape.n_q_heads, D), dtype=torch.bfloat16, device=dev),
+            "ws": api.workspace(api.gemma_attn_decode_multi_workspace_size(lay, B, q_len, int(lens.max())), dev),
+            "bytes": sum(n_keys) * Hkv * D * 2 * (1 if shape.kv_shared else 2),
+        })
+
+    def step():
+        for L in layers:
+            for j in range(q_len):
+                api.kv_append(L["lay"], L["kn"][j], None if L["vn"] is None else L["vn"][j], L["g_k"], L["pos"][j],
+                              L["kc"], L["vc"])
+            api.gemma_attn_decode_multi(L["lay"], L["q"], L["g_q"], L["kc"], L["vc"], L["seq"], L["max"],
+                                        L["out"], L["ws"])
+
+    steps = max(args.decode_steps // 2, 8)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sec = timed(step, steps, 0, torch)
+    nbytes = sum(L["bytes"] for L in layers)
+    del layers
+    torch.cuda.empty_cache()
+    gbs = nbytes / sec / 1e9
+    return {
+        "workload": f"6-layer verification step of {q_len} drafted tokens per sequence: 5 local (32q/16kv, d=256, "
+                    f"W=1024, ring of {1024 + q_len - 1} slots) + 1 global K=V (32q/4kv, d=512), B=32, context "
+                    "65536, per layer kv_append of each token then one multi-token decode",
+        "q_len": q_len, "ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(B * q_len / sec, 1),
+        "kv_bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s", "steps": steps,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / MI355X_HBM_GBS, 4)},
+    }
+
+
 def cpu_baseline(pre, budget_s, torch):
     """The oracle as it stands, on a bounded sample of the same prefill."""
     import oracle as O
@@ -634,6 +694,8 @@ def main():
         line["local_prefill"] = bench_local_prefill(args, torch, api, W)
     if not args.no_stack:
         line["stack_decode"] = bench_stack_decode(args, torch, api, W)
+    if not args.no_verify:
+        line["stack_verify"] = bench_stack_verify(args, torch, api, W)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds, torch)
         if not args.no_decode and cpu_dec is not None:

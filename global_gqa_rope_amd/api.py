@@ -219,19 +219,22 @@ def gemma_attn_prefill_chunk_workspace_size(layer: Layer, batch: int, start: int
 
 
 def gemma_attn_prefill_chunk(layer: Layer, start: int, q, k, q_gain, k_gain, k_cache, out=None, ws=None,
-                             stream=None) -> torch.Tensor:
-    """Positions start .. start + chunk - 1 against k_cache slots 0 .. start - 1 (global K=V layers)."""
+                             stream=None, v=None, v_cache=None) -> torch.Tensor:
+    """Positions start .. start + chunk - 1 against the positions already in the caches."""
     B, T, Hq, d = q.shape
     Hkv = layer.n_kv_heads
     kc, cap = _cache(layer, k_cache, "k_cache", B)
+    vc, vcap = _cache(layer, v_cache, "v_cache", B)
+    if v_cache is not None and vcap != cap:
+        raise ValueError("k_cache and v_cache differ in capacity")
     if out is None:
         out = _on_stream(torch.empty_like(q), stream)
     if ws is None:
         ws = _on_stream(workspace(gemma_attn_prefill_chunk_workspace_size(layer, B, start, T), q.device), stream)
     st = _lib.load().gemma_attn_prefill_chunk(
         ctypes.byref(layer.struct()), B, int(start), T, _ptr(q, "q", layer, (B, T, Hq, d)),
-        _ptr(k, "k", layer, (B, T, Hkv, d)), _ptr(q_gain, "q_gain", layer, (d,)),
-        _ptr(k_gain, "k_gain", layer, (d,)), kc, cap,
+        _ptr(k, "k", layer, (B, T, Hkv, d)), _ptr(v, "v", layer, (B, T, Hkv, d)),
+        _ptr(q_gain, "q_gain", layer, (d,)), _ptr(k_gain, "k_gain", layer, (d,)), kc, vc, cap,
         _ptr(out, "out", layer, (B, T, Hq, d)), _ptr(ws, "workspace", dtype=torch.uint8), ws.numel(),
         _stream(stream))
     _lib.check(st)

@@ -144,8 +144,9 @@ ga_status check_caches(const ga_layer* L, const void* k_cache, const void* v_cac
     return fail(GA_EINVAL, "layer with a separate V needs v_cache");
   }
   if (L->window > 0) {
-    if (cache_cap != L->window)
-      return fail(GA_EINVAL, "windowed layer: cache_cap (%d) must equal window (%d)", cache_cap, L->window);
+    if (cache_cap < L->window)
+      return fail(GA_EINVAL, "windowed layer: cache_cap (%d) must be at least the window (%d)", cache_cap,
+                  L->window);
   } else if (cache_cap < min_cap) {
     return fail(GA_EINVAL, "cache_cap (%d) is smaller than the sequence (%d)", cache_cap, min_cap);
   }
@@ -195,8 +196,11 @@ PrefillLayout prefill_layout(const ga_layer* L, const Derived& dv, int batch, in
   return p;
 }
 
-int decode_tiles_per_seq(const ga_layer* L, int max_seq_len) {
-  const int keys = L->window > 0 ? std::min(max_seq_len, L->window) : max_seq_len;
+// Tiles of one (sequence, KV head) segment at most: windowed layers read the
+// min(L, cache_cap) filled ring slots; cache_cap = 0 (the size queries, which
+// do not take it) bounds them by max_seq_len.
+int decode_tiles_per_seq(const ga_layer* L, int max_seq_len, int cache_cap) {
+  const int keys = (L->window > 0 && cache_cap > 0) ? std::min(max_seq_len, cache_cap) : max_seq_len;
   return (keys + ga::kDecodeTile - 1) / ga::kDecodeTile;
 }
 
@@ -205,28 +209,25 @@ int decode_tiles_per_seq(const ga_layer* L, int max_seq_len) {
 // depend on the device; the launch then uses one workgroup per CU at most.
 constexpr int kMaxDecodeCUs = 1 << 20;
 
-bool decode_plan(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len, int n_cus,
-                 ga::DecodePlan* plan) {
+bool decode_plan(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len, int cache_cap,
+                 int n_cus, ga::DecodePlan* plan) {
   return ga::plan_decode(L->dtype, L->head_dim, dv.group, L->kv_shared, batch, L->n_kv_heads,
-                         decode_tiles_per_seq(L, max_seq_len), n_cus, q_len, plan);
+                         decode_tiles_per_seq(L, max_seq_len, cache_cap), n_cus, q_len, plan);
 }
 
 size_t decode_bytes(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len) {
   ga::DecodePlan plan;
-  if (!decode_plan(L, dv, batch, q_len, max_seq_len, kMaxDecodeCUs, &plan)) return 0;
+  if (!decode_plan(L, dv, batch, q_len, max_seq_len, 0, kMaxDecodeCUs, &plan)) return 0;
   return align_up(plan.bytes());
 }
 
 // The query tokens of one decode call fill the 16 columns of the QK^T MFMA:
-// q_len tokens x G heads must fit.  Several tokens at once are built for the
-// global K=V layers; a windowed layer's ring of W slots no longer holds keys
-// that an earlier one of several new tokens would see.
+// q_len tokens x G heads must fit.
 ga_status check_q_len(const ga_layer* L, const Derived& dv, int q_len) {
+  (void)L;
   if (q_len < 1) return fail(GA_EINVAL, "q_len must be >= 1");
   if (q_len * dv.group > 16)
     return fail(GA_EUNSUPPORTED, "q_len %d x %d query heads per KV head exceeds 16 query columns", q_len, dv.group);
-  if (q_len > 1 && (L->window > 0 || !L->kv_shared))
-    return fail(GA_EUNSUPPORTED, "q_len > 1 is built for global K=V layers only");
   return GA_OK;
 }
 
@@ -314,7 +315,7 @@ ga_status decode_impl(const ga_layer* layer, int32_t batch, int32_t q_len, const
   if (st != GA_OK) return st;
   if (batch == 0) return GA_OK;
   if (max_seq_len < 1) return fail(GA_EINVAL, "max_seq_len must be >= 1");
-  if (static_cast<int64_t>(batch) * layer->n_kv_heads * decode_tiles_per_seq(layer, max_seq_len) > INT32_MAX)
+  if (static_cast<int64_t>(batch) * layer->n_kv_heads * decode_tiles_per_seq(layer, max_seq_len, 0) > INT32_MAX)
     return fail(GA_EUNSUPPORTED, "batch %d x max_seq_len %d: too many cached positions for one decode call", batch,
                 max_seq_len);
   if (!q || !q_gain || !seq_lens || !out) return fail(GA_EINVAL, "q, q_gain, seq_lens and out must be non-NULL");
@@ -322,6 +323,10 @@ ga_status decode_impl(const ga_layer* layer, int32_t batch, int32_t q_len, const
     return fail(GA_EUNSUPPORTED, "fp32 decode with head_dim 512 and a separate V cache is not built");
   st = check_caches(layer, k_cache, v_cache, cache_cap, false, 1);
   if (st != GA_OK) return st;
+  if (layer->window > 0 && q_len > 1 && cache_cap < layer->window + q_len - 1)
+    return fail(GA_EINVAL, "windowed layer: %d new tokens at once need a ring of window + %d = %d slots (cache_cap "
+                "%d); the earliest of them still sees keys the later ones push out of a smaller ring", q_len,
+                q_len - 1, layer->window + q_len - 1, cache_cap);
   if (static_cast<int64_t>(cache_cap) * layer->head_dim * (dv.q8 ? 1 : dv.elem) > INT32_MAX)
     return fail(GA_EUNSUPPORTED, "cache_cap %d: one head's cache must stay under 2 GiB for decode", cache_cap);
   if (reinterpret_cast<uintptr_t>(k_cache) % 16 || reinterpret_cast<uintptr_t>(v_cache) % 16)
@@ -335,7 +340,7 @@ ga_status decode_impl(const ga_layer* layer, int32_t batch, int32_t q_len, const
   if (he == hipSuccess) he = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (he != hipSuccess) return hip_status(he, "decode: device query");
   ga::DecodePlan plan;
-  if (!decode_plan(layer, dv, batch, q_len, max_seq_len, cus, &plan))
+  if (!decode_plan(layer, dv, batch, q_len, max_seq_len, cache_cap, cus, &plan))
     return fail(GA_EUNSUPPORTED, "no decode kernel for this layer configuration");
   if (noalloc) {
     if (plan.bytes() > kNoAllocScratchBytes)
@@ -422,8 +427,9 @@ size_t gemma_attn_decode_multi_workspace_size(const ga_layer* layer, int32_t bat
 }
 
 // Prefill of positions start .. start + seq_len - 1 of every sequence.  start
-// > 0 (global K=V layers): positions 0 .. start - 1 are in k_cache already and
-// are read back into the workspace rows.
+// > 0: positions before start are in the caches already (K=V and separate-V
+// global layers: slot = position; windowed layers: their ring) and are read
+// back into the workspace rows.
 static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t start, int32_t seq_len, const void* q,
                               const void* k, const void* v, const void* q_gain, const void* k_gain, void* k_cache,
                               void* v_cache, int32_t cache_cap, void* out, void* workspace, size_t workspace_bytes,
@@ -437,11 +443,8 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
   if ((total + ga::kPrepTile) * layer->head_dim * dv.elem > INT32_MAX)
     return fail(GA_EUNSUPPORTED, "seq_len %lld: one head's key tiles must stay under 2 GiB",
                 static_cast<long long>(total));
-  if (start > 0) {
-    if (!layer->kv_shared || layer->window > 0)
-      return fail(GA_EUNSUPPORTED, "a prefill chunk after cached positions is built for global K=V layers only");
-    if (!k_cache) return fail(GA_EINVAL, "a prefill chunk after cached positions needs the k_cache holding them");
-  }
+  if (start > 0 && !k_cache)
+    return fail(GA_EINVAL, "a prefill chunk after cached positions needs the caches holding them");
   if (batch == 0 || seq_len == 0) return GA_OK;
   if (!q || !k || !q_gain || !k_gain || !out) return fail(GA_EINVAL, "q, k, q_gain, k_gain and out must be non-NULL");
   if (layer->kv_shared && v) return fail(GA_EINVAL, "K=V layer: v must be NULL (keys are the values)");
@@ -459,26 +462,41 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  // Separate-V layers: the attention kernel reads v in place when one head's
-  // rows (Hkv d elements apart) span less than 2^31 bytes; else prep copies it
-  // into the workspace rows.
-  const bool v_in_place = !layer->kv_shared &&
+  // Separate-V layers: the attention kernel reads v in place when the prompt
+  // is whole and one head's rows (Hkv d elements apart) span less than 2^31
+  // bytes; else prep copies v (and the cached values) into the workspace rows.
+  const bool v_in_place = !layer->kv_shared && start == 0 &&
       static_cast<int64_t>(seq_len) * layer->n_kv_heads * layer->head_dim * dv.elem < (int64_t{1} << 31);
+  // Windowed layers read only the window before the chunk's first position.
+  const int tile0 = layer->window > 0 ? std::max(0, start - layer->window + 1) / ga::kPrepTile : 0;
+  // A windowed chunk reads ring slots that its own rows overwrite: the ring
+  // is written by a second pass, after every read.
+  const bool ring_after = layer->window > 0 && start > 0;
   {
     ProfScope ps(s, 1);
-    st = hip_status(ga::launch_rope_table(ws + lay.table, lay.seq_pad, dv.n_rot, layer->head_dim, dv.log2_theta, s),
+    st = hip_status(ga::launch_rope_table(ws + lay.table, tile0 * ga::kPrepTile, lay.seq_pad, dv.n_rot,
+                                          layer->head_dim, dv.log2_theta, s),
                     "rope table launch");
-    if (st == GA_OK) {
-      ga::PrepArgs pa{};
-      pa.k = k; pa.v = v; pa.k_gain = k_gain; pa.rope_table = ws + lay.table;
-      pa.k_cache = k_cache; pa.v_cache = v_cache; pa.ws_k = ws + lay.ws_k; pa.ws_v = ws + lay.ws_v; pa.kw = lay.kw;
-      pa.seq_len = seq_len; pa.seq_pad = lay.seq_pad; pa.n_kv_heads = layer->n_kv_heads; pa.n_rot = dv.n_rot;
-      pa.window = layer->window; pa.kv_shared = layer->kv_shared; pa.cache_cap = cache_cap; pa.eps = layer->norm_eps;
-      pa.pos0 = start;
-      pa.write_v = !layer->kv_shared && !v_in_place;
-      pa.k_scales = q8_scales(layer, dv, k_cache, batch, cache_cap);
-      pa.k_heads = pre_heads(layer, dv, k_cache, batch, cache_cap);
+    ga::PrepArgs pa{};
+    pa.k = k; pa.v = v; pa.k_gain = k_gain; pa.rope_table = ws + lay.table;
+    pa.k_cache = k_cache; pa.v_cache = v_cache; pa.ws_k = ws + lay.ws_k; pa.ws_v = ws + lay.ws_v; pa.kw = lay.kw;
+    pa.seq_len = seq_len; pa.seq_pad = lay.seq_pad; pa.n_kv_heads = layer->n_kv_heads; pa.n_rot = dv.n_rot;
+    pa.window = layer->window; pa.kv_shared = layer->kv_shared; pa.cache_cap = cache_cap; pa.eps = layer->norm_eps;
+    pa.pos0 = start;
+    pa.tile0 = tile0;
+    pa.write_v = !layer->kv_shared && !v_in_place;
+    pa.write_ws = 1;
+    pa.write_cache = !ring_after;
+    pa.k_scales = q8_scales(layer, dv, k_cache, batch, cache_cap);
+    pa.k_heads = pre_heads(layer, dv, k_cache, batch, cache_cap);
+    if (st == GA_OK)
       st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "prefill prep launch");
+    if (st == GA_OK && ring_after && k_cache) {
+      // the chunk's last cache_cap positions into the ring
+      pa.write_ws = 0;
+      pa.write_cache = 1;
+      pa.tile0 = static_cast<int>(std::max<int64_t>(start, total - cache_cap) / ga::kPrepTile);
+      st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "ring write launch");
     }
   }
   if (st != GA_OK) return st;
@@ -512,10 +530,10 @@ size_t gemma_attn_prefill_chunk_workspace_size(const ga_layer* layer, int32_t ba
 }
 
 ga_status gemma_attn_prefill_chunk(const ga_layer* layer, int32_t batch, int32_t start, int32_t chunk,
-                                   const void* q, const void* k, const void* q_gain, const void* k_gain,
-                                   void* k_cache, int32_t cache_cap, void* out, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
-  return prefill_impl(layer, batch, start, chunk, q, k, nullptr, q_gain, k_gain, k_cache, nullptr, cache_cap, out,
+                                   const void* q, const void* k, const void* v, const void* q_gain,
+                                   const void* k_gain, void* k_cache, void* v_cache, int32_t cache_cap, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(layer, batch, start, chunk, q, k, v, q_gain, k_gain, k_cache, v_cache, cache_cap, out,
                       workspace, workspace_bytes, stream);
 }
 

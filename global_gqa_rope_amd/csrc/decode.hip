@@ -125,11 +125,13 @@ template <int N>
 __device__ __forceinline__ void wait_vm_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // Sequence b's number of readable keys, or -1 if its length is out of range.
+// Global layers read slots 0 .. L-1 (slot = position); windowed layers the
+// min(L, cache_cap) filled slots of their ring (slot = position mod cache_cap).
 __device__ __forceinline__ int decode_keys(const DecodeArgs& a, int b) {
   const int L = a.seq_lens[b];
   if (L < a.q_len || L < 1 || L > a.max_seq_len) return -1;
   if (a.window == 0 && L > a.cache_cap) return -1;
-  return a.window > 0 ? min(L, a.window) : L;
+  return a.window > 0 ? min(L, a.cache_cap) : L;
 }
 
 // Key rows sit in LDS in natural order [key][d]; 16-byte chunk c of row r is
@@ -592,8 +594,16 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
 #pragma unroll
     for (int t = 0; t < C::kDBlocks; ++t) o[t] = f32x4{};
     float m_run = -INFINITY, l_part = 0.f;
-    // keys the lane's column sees: token j of q_len sits at position L - q_len + j
+    // Keys the lane's column sees: token j of q_len sits at position
+    // P = L - q_len + j.  Global layers (slot = position): slots below
+    // key_lim = P + 1.  Windowed layers: slot s of the ring holds position
+    // base + s, or base + s - cache_cap past the newest slot h = (L - 1) mod
+    // cache_cap, and is seen when P - W < position <= P.
     const int key_lim = cur.keys - ((hcol < ncol) ? a.q_len - 1 - hcol / G : 0);
+    const int L_cur = a.seq_lens[cur.b];
+    const int col_pos = L_cur - a.q_len + ((hcol < ncol) ? hcol / G : a.q_len - 1);
+    const int ring_h = a.window > 0 ? (L_cur - 1) % a.cache_cap : 0;
+    const int ring_base = L_cur - 1 - ring_h;
 
     for (;; ++k) {
       const int g = t_begin + wave + C::kWaves * k;
@@ -655,11 +665,20 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
 
         // online softmax; lane holds keys 4*kg + v of head column hcol
         float mt = -INFINITY;
+        if (a.window > 0) {
   #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (key0 + 4 * kg + v >= key_lim) s[v] = -INFINITY;
-          mt = fmaxf(mt, s[v]);
+          for (int v = 0; v < 4; ++v) {
+            const int slot = key0 + 4 * kg + v;
+            const int p = ring_base + slot - (slot > ring_h ? a.cache_cap : 0);
+            if (slot >= cur.keys || p > col_pos || p <= col_pos - a.window) s[v] = -INFINITY;
+          }
+        } else {
+  #pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (key0 + 4 * kg + v >= key_lim) s[v] = -INFINITY;
         }
+  #pragma unroll
+        for (int v = 0; v < 4; ++v) mt = fmaxf(mt, s[v]);
         mt = max_across_kg(mt);
         const bool rescale = __any(mt > m_run + kTau);
         const float m_new = rescale ? fmaxf(m_run, mt) : m_run;

@@ -32,8 +32,11 @@ struct PrepArgs {
   void* ws_k;              // [B][Hkv][seq_pad][kw] rotated normalised keys
   void* ws_v;              // [B][Hkv][seq_pad][d] value rows
   int seq_len, seq_pad, n_kv_heads, n_rot, window, kv_shared, cache_cap, kw;
-  int pos0;                // position of k's first row; rows 0 .. pos0-1 come from the K=V cache
+  int pos0;                // position of k's first row; rows 0 .. pos0-1 come from the caches
+  int tile0;               // first tile of kPrepTile positions to prepare (earlier rows are not read)
   int write_v;             // separate-V layers: copy v into ws_v (the attention kernel reads it there)
+  int write_ws;            // write the key and value rows of the workspace
+  int write_cache;         // write the new rows into the caches
   float* k_scales;         // int8 K=V cache: per-row scales [B][Hkv][cache_cap] (else null)
   void* k_heads;           // pre-rotated K=V cache: heads [B][Hkv][cache_cap][2 n_rot] (else null)
   float eps;
@@ -99,7 +102,7 @@ struct DecodePlan {
 bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, int n_kv_heads,
                  int max_tiles_per_seq, int n_cus, int q_len, DecodePlan* plan);
 
-hipError_t launch_rope_table(void* table, int n_pos, int n_rot, int head_dim, double log2_theta,
+hipError_t launch_rope_table(void* table, int pos_begin, int n_pos, int n_rot, int head_dim, double log2_theta,
                              hipStream_t s);
 hipError_t launch_prefill_prep(const PrepArgs& a, int dtype, int head_dim, int batch, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, int dtype, int head_dim, int batch, hipStream_t s);

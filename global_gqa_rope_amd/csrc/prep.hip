@@ -6,10 +6,12 @@
 namespace ga {
 
 // table[pos][pair] = (cos, sin)(pos * theta^(-2 pair / d)), fp64 math.
-__global__ void rope_table_kernel(f32x2* __restrict__ table, int n_pos, int n_rot,
+// Rows pos_begin .. n_pos - 1 (earlier rows are not read).
+__global__ void rope_table_kernel(f32x2* __restrict__ table, int pos_begin, int n_pos, int n_rot,
                                   int head_dim, double log2_theta) {
+  const int64_t first = static_cast<int64_t>(pos_begin) * n_rot;
   const int64_t total = static_cast<int64_t>(n_pos) * n_rot;
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
+  for (int64_t i = first + blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int pos = static_cast<int>(i / n_rot);
     const int pair = static_cast<int>(i % n_rot);
@@ -35,14 +37,26 @@ __device__ __forceinline__ void q8_unpack8(float (&x)[8], uint2 u, float s) {
     x[j] = static_cast<float>(static_cast<int8_t>((j < 4 ? u.x : u.y) >> (8 * (j % 4)))) * s;
 }
 
-// One workgroup per (tile of kPrepTile key positions, kv head, batch).
+// One workgroup per (tile of kPrepTile key positions, kv head, batch), for the
+// tiles tile0 .. seq_pad / kPrepTile - 1 (earlier rows are never read).
 // Thread t owns key row r = t / 8 of the tile and the 8-element chunks
 // i * 8 + t % 8 of that row, so eight neighbouring lanes cover 64 contiguous
 // elements of one row.  Every global access is a 16-byte vector, and all
-// loads of a thread are issued before the first use.  Positions pos0 ..
-// pos0 + seq_len - 1 are k's rows; on K=V layers positions below pos0 are
-// already in the cache (a later chunk of a prompt) and are read back from it,
-// normalised and unrotated, into the key and value rows.
+// loads of a thread are issued before the first use.  A row is one of:
+//  - new (positions pos0 .. pos0 + seq_len - 1, k's rows): normalised; the key
+//    row is rotated, the value row is the normalised key (K=V) or v;
+//  - cached (a position below pos0, a later chunk of a prompt), read back from
+//    the caches: on K=V layers the stored normalised, unrotated key (int8:
+//    codes times the row scale), rotated for the key row and as stored for the
+//    value row; on separate-V layers the stored key, already normalised and
+//    rotated, and the stored value.  A windowed layer's ring holds the last
+//    cache_cap positions before pos0; older rows lie outside every new row's
+//    window and are zeros;
+//  - padding (past the sequence): zeros.
+// write_ws: write the key and value rows of the workspace.  write_cache:
+// write the new rows into the caches (windowed layers: those among the last
+// cache_cap positions, at slot position mod cache_cap; others: slot =
+// position).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   constexpr int kChunks = D / 8;             // 8-element chunks per row
@@ -52,25 +66,26 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   // Workgroup order: the KV heads of every sequence for one tile of positions
   // run together, so the tile's rows of the cos/sin table are read once into
   // L2 and then hit there, instead of once per head and sequence.
-  const int n_tiles = a.seq_pad / kPrepTile;
+  const int n_tiles = a.seq_pad / kPrepTile - a.tile0;
   const int n_seq = static_cast<int>(gridDim.x) / (a.n_kv_heads * n_tiles);
   const int h = static_cast<int>(blockIdx.x) % a.n_kv_heads;
   const int b = (static_cast<int>(blockIdx.x) / a.n_kv_heads) % n_seq;
-  const int tile = static_cast<int>(blockIdx.x) / (a.n_kv_heads * n_seq);
+  const int tile = a.tile0 + static_cast<int>(blockIdx.x) / (a.n_kv_heads * n_seq);
   const int t = threadIdx.x;
   const int r = t >> 3, c8 = t & 7;
   const int pos = tile * kPrepTile + r;
-  const bool valid = pos >= a.pos0 && pos < a.pos0 + a.seq_len;   // one of k's rows
-  const bool cached = pos < a.pos0;                                // already in the K=V cache
+  const int total = a.pos0 + a.seq_len;
+  const bool has_v = !a.kv_shared;
+  const bool valid = pos >= a.pos0 && pos < total;                 // one of k's rows
+  const bool cached = pos < a.pos0 && (a.window == 0 || pos >= a.pos0 - a.cache_cap);
+  const bool cached_sep = cached && has_v;                          // stored rotated, value in v_cache
+  const int slot = a.window > 0 ? pos % a.cache_cap : pos;
   // other positions read k's last row (then zeroed) so no load leaves the tensor
   const int src_pos = valid ? pos - a.pos0 : a.seq_len - 1;
   const int64_t src_row = ((static_cast<int64_t>(b) * a.seq_len + src_pos) * a.n_kv_heads + h) * D;
-  const bool has_v = !a.kv_shared;
   const int64_t head_base = (static_cast<int64_t>(b) * a.n_kv_heads + h);
-  // separate-V layers: the row goes to the caches (windowed: the last W positions)
-  const bool v_to_cache = has_v && a.k_cache && valid && (a.window == 0 || pos >= a.seq_len - a.window);
-  // v is read where it is copied: ws_v (when the attention kernel reads it there) or the caches
-  const bool need_v = has_v && (a.write_v || v_to_cache);
+  const bool to_cache = a.write_cache && a.k_cache && valid && (a.window == 0 || pos >= total - a.cache_cap);
+  const bool v_to_ws = has_v && a.write_ws && a.write_v;
 
   const T* __restrict__ k = static_cast<const T*>(a.k);
   const T* __restrict__ v = static_cast<const T*>(a.v);
@@ -79,7 +94,8 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
 
   vec8 kin[kMine], vin[kMine], gin[kMine];
   f32x2 cs[kMine][4];
-  const T* __restrict__ cache_row = static_cast<const T*>(a.k_cache) + (head_base * a.cache_cap + pos) * D;
+  const T* __restrict__ cache_row = static_cast<const T*>(a.k_cache) + (head_base * a.cache_cap + slot) * D;
+  const T* __restrict__ vcache_row = static_cast<const T*>(a.v_cache) + (head_base * a.cache_cap + slot) * D;
   const bool q8 = a.k_scales != nullptr;                  // int8 K=V cache
   const uint8_t* __restrict__ code_row = static_cast<const uint8_t*>(a.k_cache) + (head_base * a.cache_cap + pos) * D;
   uint2 qin[kMine];
@@ -90,7 +106,10 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
     if (cached && q8) qin[i] = *reinterpret_cast<const uint2*>(code_row + d0);
     else kin[i] = *reinterpret_cast<const vec8*>((cached ? cache_row : k + src_row) + d0);
     gin[i] = *reinterpret_cast<const vec8*>(gk + d0);
-    if (need_v) vin[i] = *reinterpret_cast<const vec8*>(v + src_row + d0);
+    if (has_v) {
+      if (cached_sep) vin[i] = *reinterpret_cast<const vec8*>(vcache_row + d0);
+      else if (valid && (v_to_ws || to_cache)) vin[i] = *reinterpret_cast<const vec8*>(v + src_row + d0);
+    }
   }
   if (cached && q8) q_scale = a.k_scales[head_base * a.cache_cap + pos];
   // (cos, sin) of the chunk's four pairs; pairs >= n_rot read a clamped entry
@@ -134,9 +153,9 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
   T* __restrict__ wv = static_cast<T*>(a.ws_v) + row * D;
 
   // Value row.  K=V: the normalised, unrotated key, which is also what the
-  // cache keeps (int8 caches: its codes and the row's scale).  Otherwise the
-  // raw v (zeros past the sequence).
-  if (!has_v && q8 && kc && valid) {
+  // cache keeps (int8 caches: its codes and the row's scale).  Otherwise v
+  // (the stored value for cached rows, zeros for padding).
+  if (!has_v && q8 && to_cache) {
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < kMine; ++i)
@@ -157,32 +176,34 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
     const int d0 = (i * 8 + c8) * 8;
     if (has_v) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vout[i][j] = valid ? vin[i][j] : from_f32<T>(0.f);
+      for (int j = 0; j < 8; ++j) vout[i][j] = (valid || cached) ? vin[i][j] : from_f32<T>(0.f);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) vout[i][j] = from_f32<T>(x[i][j]);
-      if (kc && valid && !q8) *reinterpret_cast<vec8*>(kc + (head_base * a.cache_cap + pos) * D + d0) = vout[i];
+      if (to_cache && !q8) *reinterpret_cast<vec8*>(kc + (head_base * a.cache_cap + pos) * D + d0) = vout[i];
     }
-    if (!has_v || a.write_v) *reinterpret_cast<vec8*>(wv + d0) = vout[i];
+    if (a.write_ws && (!has_v || a.write_v)) *reinterpret_cast<vec8*>(wv + d0) = vout[i];
   }
 
-  // Rotate the first 2*n_rot dims.
+  // Rotate the first 2*n_rot dims (cached separate-V keys are stored rotated).
+  if (!cached_sep) {
 #pragma unroll
-  for (int i = 0; i < kMine; ++i) {
-    const int d0 = (i * 8 + c8) * 8;
+    for (int i = 0; i < kMine; ++i) {
+      const int d0 = (i * 8 + c8) * 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (d0 / 2 + j < a.n_rot) rotate_pair(x[i][2 * j], x[i][2 * j + 1], cs[i][j]);
+      for (int j = 0; j < 4; ++j) {
+        if (d0 / 2 + j < a.n_rot) rotate_pair(x[i][2 * j], x[i][2 * j + 1], cs[i][j]);
+      }
     }
   }
   vec8 kout[kMine];
 #pragma unroll
   for (int i = 0; i < kMine; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kout[i][j] = from_f32<T>(x[i][j]);
+    for (int j = 0; j < 8; ++j) kout[i][j] = cached_sep ? kin[i][j] : from_f32<T>(x[i][j]);
 
   // Key row: dims 0..kw-1 of the rotated normalised key.
-  {
+  if (a.write_ws) {
     T* __restrict__ wk = static_cast<T*>(a.ws_k) + row * a.kw;
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
@@ -193,7 +214,7 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
 
   // Pre-rotated K=V caches also keep each new row's rotated head
   // (dims 0 .. 2 n_rot - 1, as the key row above).
-  if (a.k_heads && valid) {
+  if (a.k_heads && to_cache) {
     T* __restrict__ hk = static_cast<T*>(a.k_heads) + (head_base * a.cache_cap + pos) * (2 * a.n_rot);
 #pragma unroll
     for (int i = 0; i < kMine; ++i) {
@@ -202,11 +223,10 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
     }
   }
 
-  // Separate-V layers: windowed ones keep the last W positions in a ring of
-  // cache_cap = W slots, global ones every position (slot = position); keys
-  // rotated.
-  if (v_to_cache) {
-    const int slot = a.window > 0 ? pos % a.cache_cap : pos;
+  // Separate-V layers: windowed ones keep the last cache_cap positions in a
+  // ring (slot = position mod cache_cap), global ones every position (slot =
+  // position); keys rotated.
+  if (has_v && to_cache) {
     T* dk = kc + (head_base * a.cache_cap + slot) * D;
     T* dv = vc + (head_base * a.cache_cap + slot) * D;
 #pragma unroll
@@ -298,18 +318,20 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
 
 // ---- launchers ---------------------------------------------------------------
 
-hipError_t launch_rope_table(void* table, int n_pos, int n_rot, int head_dim, double log2_theta,
+hipError_t launch_rope_table(void* table, int pos_begin, int n_pos, int n_rot, int head_dim, double log2_theta,
                              hipStream_t s) {
-  if (n_rot == 0 || n_pos == 0) return hipSuccess;
-  const int64_t total = static_cast<int64_t>(n_pos) * n_rot;
+  if (n_rot == 0 || n_pos <= pos_begin) return hipSuccess;
+  const int64_t total = static_cast<int64_t>(n_pos - pos_begin) * n_rot;
   const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 4096));
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, static_cast<f32x2*>(table),
-                     n_pos, n_rot, head_dim, log2_theta);
+                     pos_begin, n_pos, n_rot, head_dim, log2_theta);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_prep(const PrepArgs& a, int dtype, int head_dim, int batch, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.seq_pad / kPrepTile) * a.n_kv_heads * batch);
+  const int tiles = a.seq_pad / kPrepTile - a.tile0;
+  if (tiles <= 0 || batch == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tiles) * a.n_kv_heads * batch);
   if (dtype == 0 && head_dim == 512) hipLaunchKernelGGL((prefill_prep_kernel<bf16, 512>), grid, dim3(256), 0, s, a);
   else if (dtype == 0 && head_dim == 256) hipLaunchKernelGGL((prefill_prep_kernel<bf16, 256>), grid, dim3(256), 0, s, a);
   else if (dtype == 1 && head_dim == 512) hipLaunchKernelGGL((prefill_prep_kernel<float, 512>), grid, dim3(256), 0, s, a);

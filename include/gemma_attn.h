@@ -27,8 +27,9 @@
  *     = position j; p-RoPE is applied on the fly when scores are formed and the
  *     unrotated tensor is the value;
  *   - layers with a separate V: the K cache holds normalised and ROTATED keys and
- *     the V cache the raw values; windowed layers keep a ring of W slots
- *     (slot = position mod W).
+ *     the V cache the raw values; windowed layers keep a ring of cache_cap >= W
+ *     slots (slot = position mod cache_cap).  W slots hold every key the newest
+ *     token sees; checking q_len new tokens at once needs W + q_len - 1.
  *
  * Ownership and execution:
  *   - every pointer argument is caller-owned DEVICE memory except `layer`
@@ -135,8 +136,8 @@ size_t gemma_attn_prefill_workspace_size(const ga_layer* layer, int32_t batch,
  *   q_gain, k_gain [d]      QKNorm gains
  *   k_cache [B, Hkv, cache_cap, d] or NULL (no cache write).
  *           K=V: slots 0..S-1 receive the normalised unrotated keys; needs
- *           cache_cap >= S.  Windowed: ring of cache_cap == W slots receiving
- *           the normalised rotated keys of positions max(0, S-W)..S-1.
+ *           cache_cap >= S.  Windowed: ring of cache_cap >= W slots receiving
+ *           the normalised rotated keys of positions max(0, S-cache_cap)..S-1.
  *   v_cache like k_cache; windowed separate-V layers only (else NULL); gets v.
  *   out     [B, S, Hq, d]
  *   q, k, v, the gains, the caches and out are read and written in 16-byte
@@ -179,29 +180,34 @@ ga_status kv_append(const ga_layer* layer, int32_t batch,
                     int32_t cache_cap, void* stream);
 
 /*
- * Prefill of a later chunk of a prompt against the positions already cached
- * (global K=V layers): positions start .. start + chunk - 1 of each sequence
- * attend causally to positions 0 .. their own, where k_cache slots
- * 0 .. start - 1 hold the earlier positions (as a prefill or kv_append wrote
- * them).  The chunk's keys are normalised into slots start .. start + chunk - 1.
- * Each output row is the row a prefill of the whole prompt would give; this is
- * the longer form of checking many new tokens at once (see
- * gemma_attn_decode_multi).
+ * Prefill of a later chunk of a prompt against the positions already cached:
+ * positions start .. start + chunk - 1 of each sequence attend causally (and
+ * within the window on windowed layers) to positions 0 .. their own.  The
+ * earlier positions come from the caches as a prefill, an earlier chunk or
+ * kv_append wrote them: K=V and separate-V global layers from slots
+ * 0 .. start - 1, windowed layers from their ring (which holds the last
+ * cache_cap >= W positions before start, so every key the chunk sees).  The
+ * chunk's keys (and values) are then written as gemma_attn_prefill writes
+ * them: slots start .. start + chunk - 1, or the ring's slots of the last
+ * cache_cap positions of the chunk.  Each output row is the row a prefill of
+ * the whole prompt would give; this is also the longer form of checking many
+ * new tokens at once (see gemma_attn_decode_multi).
  *
- *   q [B, chunk, Hq, d], k [B, chunk, Hkv, d] raw; out [B, chunk, Hq, d]
- *   k_cache [B, Hkv, cache_cap, d], cache_cap >= start + chunk
+ *   q [B, chunk, Hq, d], k [B, chunk, Hkv, d] raw; v [B, chunk, Hkv, d] raw on
+ *   layers with a separate V (NULL on K=V layers); out [B, chunk, Hq, d]
+ *   k_cache, v_cache [B, Hkv, cache_cap, d]: global layers cache_cap >= start +
+ *   chunk, windowed layers cache_cap >= W; v_cache NULL on K=V layers
  *   workspace >= gemma_attn_prefill_chunk_workspace_size() bytes, 256-byte
  *   aligned (the workspace of a prefill of start + chunk positions).
- * start = 0 is gemma_attn_prefill with a cache.  GA_EUNSUPPORTED for start > 0
- * on a layer other than a global K=V one; other errors as for
- * gemma_attn_prefill.
+ * start = 0 is gemma_attn_prefill with the caches.  GA_EINVAL for start > 0
+ * without k_cache; other errors as for gemma_attn_prefill.
  */
 size_t gemma_attn_prefill_chunk_workspace_size(const ga_layer* layer, int32_t batch,
                                                int32_t start, int32_t chunk);
 ga_status gemma_attn_prefill_chunk(const ga_layer* layer, int32_t batch, int32_t start,
-                                   int32_t chunk, const void* q, const void* k,
+                                   int32_t chunk, const void* q, const void* k, const void* v,
                                    const void* q_gain, const void* k_gain, void* k_cache,
-                                   int32_t cache_cap, void* out, void* workspace,
+                                   void* v_cache, int32_t cache_cap, void* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
 /*
@@ -233,8 +239,9 @@ size_t gemma_attn_decode_workspace_size(const ga_layer* layer, int32_t batch,
  *   k_cache, v_cache, cache_cap: as written by prefill / kv_append (v_cache
  *            NULL when kv_shared = 1)
  *   seq_lens device int32 [B]: valid keys including the new token (L_b >= 1).
- *            K=V layers read slots 0..L_b-1; windowed layers the min(L_b, W)
- *            filled ring slots.
+ *            Global layers read slots 0..L_b-1; windowed layers the
+ *            min(L_b, cache_cap) filled ring slots, of which those inside the
+ *            window are seen.
  *   max_seq_len host bound on every seq_lens[b], sizes the workspace.  A
  *            sequence with L_b < 1, L_b > max_seq_len or (K=V) L_b > cache_cap
  *            gets a NaN output row instead of reading out of bounds.
@@ -266,11 +273,13 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch,
  *            sequence with L_b < q_len gets NaN rows like an invalid length.
  *   other arguments as for gemma_attn_decode, with the workspace from
  *   gemma_attn_decode_multi_workspace_size().
+ * Every layer type: global layers read slots 0 .. L_b - 1, windowed layers
+ * their ring, token j seeing the positions inside its own window.  A
+ * windowed layer needs a ring of cache_cap >= W + q_len - 1 slots (GA_EINVAL
+ * otherwise): with W slots the later new tokens would have pushed out keys
+ * the earlier ones still see.
  * q_len = 1 is gemma_attn_decode.  GA_EINVAL for q_len < 1; GA_EUNSUPPORTED
- * when q_len * (Hq / Hkv) > 16 (the query columns of one pass) or when
- * q_len > 1 on a layer other than a global K=V one (a windowed layer's ring
- * of W slots has already dropped keys that the earlier of the new tokens
- * would see).
+ * when q_len * (Hq / Hkv) > 16 (the query columns of one pass).
  */
 size_t gemma_attn_decode_multi_workspace_size(const ga_layer* layer, int32_t batch,
                                               int32_t q_len, int32_t max_seq_len);

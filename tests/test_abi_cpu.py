@@ -81,8 +81,8 @@ def test_prefill_argument_validation(lib):
     assert prefill(lib, g, v=FAKE) == 1                      # K=V takes no v
     loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
     assert prefill(lib, loc, v=None) == 1                    # local needs v
-    assert prefill(lib, loc, v=FAKE, k_cache=FAKE, v_cache=FAKE, cap=512) == 1   # ring = W
-    assert "must equal window" in lib.gemma_attn_last_error().decode()
+    assert prefill(lib, loc, v=FAKE, k_cache=FAKE, v_cache=FAKE, cap=512) == 1   # ring >= W
+    assert "at least the window" in lib.gemma_attn_last_error().decode()
     assert prefill(lib, g, k_cache=FAKE, cap=8, S=16) == 1   # cache too small
     assert prefill(lib, g, k_cache=FAKE, v_cache=FAKE, cap=64) == 1
     assert prefill(lib, g, ws=None, ws_bytes=0) == 3
@@ -127,9 +127,11 @@ def test_multi_token_decode_validation(lib):
     assert dec(T=0) == 1                                        # q_len >= 1
     assert dec(T=3) == 2                                        # 3 tokens x 8 heads > 16 columns
     assert "16 query columns" in lib.gemma_attn_last_error().decode()
-    assert dec(layer=loc, T=2, v=FAKE, cap=1024) == 2           # windowed layers take one token
+    assert dec(layer=loc, T=2, v=FAKE, cap=1024) == 1           # a W-slot ring is too small for 2 tokens
+    assert "1025 slots" in lib.gemma_attn_last_error().decode()
     wsz = lambda layer, B, T, n: lib.gemma_attn_decode_multi_workspace_size(ctypes.byref(layer), B, T, n)
-    assert wsz(g, 2, 0, 4096) == 0 and wsz(g, 2, 3, 4096) == 0 and wsz(loc, 2, 2, 4096) == 0
+    assert wsz(g, 2, 0, 4096) == 0 and wsz(g, 2, 3, 4096) == 0
+    assert wsz(loc, 2, 2, 4096) == decode_ws(2, 16, 4, 256, 4096)     # 2 tokens x G = 2 columns per slot
     # one token is the single-token call; two tokens widen every slot to 2 G d outputs
     assert wsz(g, 2, 1, 4096) == lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 4096)
     assert wsz(g, 2, 2, 4096) == decode_ws(2, 4, 16, 512, 4096)
@@ -141,9 +143,13 @@ def test_prefill_chunk_validation(lib):
     g = L()
     loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
     ch = lambda **kw: lib.gemma_attn_prefill_chunk(
-        ctypes.byref(kw.get("layer", g)), 1, kw.get("start", 64), kw.get("chunk", 16), FAKE, FAKE, FAKE, FAKE,
-        kw.get("kc", FAKE), kw.get("cap", 4096), FAKE, FAKE, 1 << 40, None)
-    assert ch(layer=loc, cap=1024) == 2                         # later chunks: global K=V layers only
+        ctypes.byref(kw.get("layer", g)), 1, kw.get("start", 64), kw.get("chunk", 16), FAKE, FAKE, kw.get("v", None),
+        FAKE, FAKE, kw.get("kc", FAKE), kw.get("vc", None), kw.get("cap", 4096), FAKE, FAKE, 1 << 40, None)
+    assert ch(layer=loc, cap=1024) == 1                         # a separate-V layer needs v
+    assert ch(layer=loc, v=FAKE, cap=1024) == 1                 # ... and v_cache
+    assert ch(layer=loc, v=FAKE, vc=FAKE, cap=1000) == 1        # a ring of at least W slots
+    assert "at least the window" in lib.gemma_attn_last_error().decode()
+    assert ch(v=FAKE) == 1                                      # K=V layers take no v
     assert ch(kc=None) == 1                                     # the cached positions live in k_cache
     assert ch(cap=79) == 1                                      # cap >= start + chunk
     assert ch(start=-1) == 1
@@ -162,8 +168,9 @@ def test_workspace_sizes_follow_the_layout(lib):
     want = s_pad * 64 * 8 + 1 * 4 * s_pad * 128 * 2 + 1 * 4 * s_pad * 512 * 2
     assert lib.gemma_attn_prefill_workspace_size(ctypes.byref(g), 1, 32768) == want
     loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
-    # a windowed layer reads at most W keys, whatever max_seq_len is
-    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(loc), 32, 65537) == decode_ws(32, 16, 2, 256, 1024)
+    # at most 1024 / waves workgroups: the scratch stops growing with max_seq_len
+    assert lib.gemma_attn_decode_workspace_size(ctypes.byref(loc), 32, 65537) == decode_ws(32, 16, 2, 256, 65537)
+    assert decode_ws(32, 16, 2, 256, 65537) == decode_ws(32, 16, 2, 256, 1024)
 
 
 def decode_ws(B, hkv, G, d, keys, waves=4):
