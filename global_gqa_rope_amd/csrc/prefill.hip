@@ -627,7 +627,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const int qh = kvh * G + (m % G);                           // query head of row m
   const bool row_valid = lpos < a.seq_len;
 
-  // ---- tile stream setup: start the first kStages - 1 copies -------------------
+  // ---- tile stream setup (the first kStages - 1 copies start in the prologue) -----
   const int p_last = min(p0 + C::QB, a.q_pos0 + a.seq_len) - 1;
   const int kt_lo = a.window > 0 ? max(0, p0 - a.window + 1) / C::KT : 0;
   const int kt_hi = p_last / C::KT + 1;
@@ -651,10 +651,6 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const uint32_t kspan = static_cast<uint32_t>(a.seq_pad) * C::kKRowBytes;   // < 2^31 (host check)
   const BufRsrc rk = make_rsrc(kbase, kspan);
   const BufRsrc rv = make_rsrc(vbase, vspan);
-#pragma unroll
-  for (int i = 0; i < C::kStages - 1; ++i)
-    issue_tile<C>(rk, rv, vstride, kt_lo + i, (lds_char*)smem + i * C::kStageBytes, wave, lane);
-
   // ---- prologue: QKNorm + rotation of query row m (this lane's half) ---------
   // bf16: the query fragments stay in registers.  fp32 would need 256
   // registers for them, so the fp32 build rebuilds each fragment from the raw
@@ -669,13 +665,31 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   float rs;
   {
     float ss = 0.f;
+    if constexpr (kQRegs) {
+      // The query loads go out before the first tiles' copies: loads
+      // complete in order, so waiting for the queries does not wait for the
+      // copies.
 #pragma unroll
-    for (int u = 0; u < C::kQSteps; ++u) {
-      Frag8<T> f;
-      load_frag(f, qrow + 16 * u + 8 * h);
+      for (int u = 0; u < C::kQSteps; ++u) load_frag(qf[u], qrow + 16 * u + 8 * h);
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss += to_f32(f.v[j]) * to_f32(f.v[j]);
-      if constexpr (kQRegs) qf[u] = f;
+      for (int i = 0; i < C::kStages - 1; ++i)
+        issue_tile<C>(rk, rv, vstride, kt_lo + i, (lds_char*)smem + i * C::kStageBytes, wave, lane);
+#pragma unroll
+      for (int u = 0; u < C::kQSteps; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += to_f32(qf[u].v[j]) * to_f32(qf[u].v[j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::kStages - 1; ++i)
+        issue_tile<C>(rk, rv, vstride, kt_lo + i, (lds_char*)smem + i * C::kStageBytes, wave, lane);
+#pragma unroll
+      for (int u = 0; u < C::kQSteps; ++u) {
+        Frag8<T> f;
+        load_frag(f, qrow + 16 * u + 8 * h);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += to_f32(f.v[j]) * to_f32(f.v[j]);
+      }
     }
     ss = sum_halves(ss);
     rs = row_valid ? (1.0f / sqrtf(ss / D + a.eps)) * a.qk_scale_log2 : 0.f;
