@@ -789,9 +789,11 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       wait_tiles<C>(C::kStages - 3);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      // copies of tiles past the workgroup's last one read nothing (an empty range)
+      const bool live = kt + C::kStages - 1 < kt_hi;
       pipe_step<C, T, D, decltype(masked)::value, true>(
-          stage_of(kt + 1), stage_of(kt), stage_of(kt + C::kStages - 1), kbase, vbase, kspan, vspan,
-          vstride, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos, a.window, st, s);
+          stage_of(kt + 1), stage_of(kt), stage_of(kt + C::kStages - 1), kbase, vbase, live ? kspan : 0u,
+          live ? vspan : 0u, vstride, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos, a.window, st, s);
     };
     const int last = kt_hi - 1;
     const int m1 = min(lo_end, last), m2 = max(m1, min(hi_begin, last));
