@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--no-prerotated", action="store_true", help="skip the pre-rotated-cache decode leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--no-calibrate", action="store_true",
+                    help="skip the measured-peak probes (an MFMA chain on random bf16 operands, a streaming read)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
     return ap.parse_args()
@@ -481,6 +483,72 @@ def bench_stack_decode(args, torch, api, W):
     }
 
 
+def calibrate(torch, api):
+    """Rates this GPU reaches on the two bounding resources: chains of 32x32x16
+    bf16 MFMAs on random operands (4 per SIMD, 4 chains each), and a streaming
+    read of 4 GiB in 16-byte loads.  Best of 5 runs, timed with events on the
+    stream the probes run on."""
+    import ctypes
+    from global_gqa_rope_amd import _lib
+    lib = _lib.load()
+    dev = torch.device("cuda", 0)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream()
+    ops = torch.randn(1 << 20, device=dev).to(torch.bfloat16)          # 131072 random 16-byte pieces
+    n_wgs, iters = 4 * cus, 4096
+    sink = torch.empty(n_wgs * 256, dtype=torch.float32, device=dev)
+
+    def run_mfma():
+        _lib.check(lib.gemma_attn_calibrate_mfma(ops.data_ptr(), ops.numel() // 8, iters, n_wgs, sink.data_ptr(),
+                                                 stream.cuda_stream))
+
+    buf = torch.randn((4 << 30) // 4, device=dev)                      # 4 GiB of random floats
+    sinku = torch.empty(8 * cus, dtype=torch.int32, device=dev)
+
+    def run_stream():
+        _lib.check(lib.gemma_attn_calibrate_stream(buf.data_ptr(), buf.numel() * 4, 8 * cus, sinku.data_ptr(),
+                                                   stream.cuda_stream))
+
+    def best_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return min(times)
+
+    mfma_ms = best_ms(run_mfma)
+    flops = n_wgs * 4 * 4 * iters * 32768.0
+    stream_ms = best_ms(run_stream)
+    nbytes = buf.numel() * 4
+    del ops, sink, buf, sinku
+    torch.cuda.empty_cache()
+    tf = flops / (mfma_ms * 1e-3) / 1e12
+    gbs = nbytes / (stream_ms * 1e-3) / 1e9
+    return {
+        "mfma_bf16": {"value": round(tf, 1), "unit": "TFLOP/s", "frac_of_published": round(tf / MI355X_BF16_DENSE_TFLOPS, 4),
+                      "probe": f"{n_wgs} workgroups x 4 waves, 4 independent chains of {iters} 32x32x16 bf16 MFMAs "
+                               "per wave on random N(0,1) operands"},
+        "hbm_read": {"value": round(gbs, 1), "unit": "GB/s", "frac_of_published": round(gbs / MI355X_HBM_GBS, 4),
+                     "probe": f"{8 * cus} workgroups read 4 GiB once, each a contiguous chunk in 16-byte loads, 8 in flight "
+                              "per lane"},
+    }
+
+
+def with_measured_peak(roof, cal):
+    """Adds the fraction of the measured peak to a roofline object."""
+    if cal is None or roof is None:
+        return
+    key = "mfma_bf16" if roof.get("bound") == "mfma" else "hbm_read"
+    roof["measured_peak"] = cal[key]["value"]
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / cal[key]["value"], 4)
+
+
 def host_info():
     """The host the oracle runs on: core counts, CPU model and the BLAS threads numpy uses."""
     model = "unknown"
@@ -696,6 +764,13 @@ def main():
         line["stack_decode"] = bench_stack_decode(args, torch, api, W)
     if not args.no_verify:
         line["stack_verify"] = bench_stack_verify(args, torch, api, W)
+    if not args.no_calibrate:
+        cal = calibrate(torch, api)
+        line["calibration"] = cal
+        with_measured_peak(line["roofline"], cal)
+        for k, v in line.items():
+            if isinstance(v, dict) and isinstance(v.get("roofline"), dict):
+                with_measured_peak(v["roofline"], cal)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds, torch)
         if not args.no_decode and cpu_dec is not None:

@@ -52,6 +52,8 @@ SIGNATURES = {
     "gemma_attn_decode_noalloc": (_I, [_LP, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P]),
     "gemma_attn_cache_bytes": (_Z, [_LP, _I, _I]),
     "gemma_attn_last_error": (ctypes.c_char_p, []),
+    "gemma_attn_calibrate_mfma": (_I, [_P, _I, _I, _I, _P, _P]),
+    "gemma_attn_calibrate_stream": (_I, [_P, _Z, _I, _P, _P]),
     "gemma_attn_version": (ctypes.c_char_p, []),
     "gemma_attn_profile_enable": (None, [ctypes.c_int]),
     "gemma_attn_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double),

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_NAME = "libgemma_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "prep.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["api.hip", "prep.hip", "prefill.hip", "decode.hip", "calibrate.hip"]
 ARCH = "gfx950"
 # Per-source device flags.  MFMAs in VGPR form: the decode kernel keeps its
 # 128 fp32 output accumulators in VGPRs and rescales them with VALU ops; the

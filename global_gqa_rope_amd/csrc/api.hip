@@ -400,6 +400,21 @@ void gemma_attn_profile_reset(void) {
 
 const char* gemma_attn_last_error(void) { return g_error.c_str(); }
 
+ga_status gemma_attn_calibrate_mfma(const void* ops, int32_t n_ops, int32_t iters, int32_t n_wgs, float* sink,
+                                    void* stream) {
+  if (!ops || !sink || n_ops <= 0 || iters <= 0 || n_wgs <= 0)
+    return fail(GA_EINVAL, "calibrate_mfma: NULL pointer or non-positive size");
+  return hip_status(ga::launch_calib_mfma(ops, n_ops, iters, n_wgs, sink, static_cast<hipStream_t>(stream)),
+                    "calibrate_mfma launch");
+}
+
+ga_status gemma_attn_calibrate_stream(const void* buf, size_t bytes, int32_t n_wgs, unsigned* sink, void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 || n_wgs <= 0)
+    return fail(GA_EINVAL, "calibrate_stream: NULL pointer, or bytes not a positive multiple of 16");
+  return hip_status(ga::launch_calib_stream(buf, bytes, n_wgs, sink, static_cast<hipStream_t>(stream)),
+                    "calibrate_stream launch");
+}
+
 const char* gemma_attn_version(void) { return "gemma_attn 0.1 (gfx950)"; }
 
 size_t gemma_attn_cache_bytes(const ga_layer* layer, int32_t batch, int32_t cache_cap) {

@@ -114,4 +114,7 @@ typedef void (*LaunchTimer)(hipStream_t, int, bool);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, int kv_shared,
                          int batch, hipStream_t s, LaunchTimer timer);
 
+hipError_t launch_calib_mfma(const void* ops, int n_ops, int iters, int n_wgs, float* sink, hipStream_t s);
+hipError_t launch_calib_stream(const void* buf, size_t bytes, int n_wgs, unsigned* sink, hipStream_t s);
+
 }  // namespace ga

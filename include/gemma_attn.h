@@ -329,6 +329,24 @@ void gemma_attn_profile_enable(int on);
 int gemma_attn_profile_read(int kernel, double* total_ms, int* count);
 void gemma_attn_profile_reset(void);
 
+/*
+ * Calibration probes (measurement only, not part of the computation): the
+ * rates this GPU reaches on the two resources the kernels above are bound by.
+ * gemma_attn_calibrate_mfma: n_wgs workgroups of 4 waves, each wave running 4
+ *   independent chains of `iters` 32x32x16 bf16 MFMAs (32768 flops each) on
+ *   operands taken from `ops` (n_ops 16-byte pieces of bf16, device); `sink`
+ *   (device, n_wgs * 256 floats) is written only to keep the chains alive.
+ * gemma_attn_calibrate_stream: n_wgs workgroups read `bytes` (a multiple of
+ *   16) of device memory at `buf` once, in 16-byte loads; `sink` (device,
+ *   n_wgs unsigned ints) as above.
+ * Both enqueue one kernel on `stream`; the caller times it.  GA_EINVAL for
+ * NULL pointers or non-positive sizes, GA_EHIP if the launch fails.
+ */
+ga_status gemma_attn_calibrate_mfma(const void* ops, int32_t n_ops, int32_t iters, int32_t n_wgs,
+                                    float* sink, void* stream);
+ga_status gemma_attn_calibrate_stream(const void* buf, size_t bytes, int32_t n_wgs, unsigned* sink,
+                                      void* stream);
+
 /* Message for the last non-OK status returned to the calling thread. */
 const char* gemma_attn_last_error(void);
 

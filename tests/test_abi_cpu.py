@@ -240,3 +240,14 @@ def test_binding_checks_cache_formats():
         api.gemma_attn_decode(q8, q, q[0, 0], c8, None, torch.zeros(2, dtype=torch.int32), 16)
     with pytest.raises(api.GemmaAttnError, match="int8 cache"):      # no int8 cache for local layers
         api.new_cache(replace(api.Layer.from_shape(W.LOCAL_LAYER, torch.bfloat16), cache_format=1), 1, 8, "cpu")
+
+
+def test_calibration_probe_validation(lib):
+    """The measurement probes reject bad arguments on the host."""
+    sink = FAKE
+    assert lib.gemma_attn_calibrate_mfma(None, 8, 4, 1, sink, None) == 1
+    assert lib.gemma_attn_calibrate_mfma(FAKE, 0, 4, 1, sink, None) == 1
+    assert lib.gemma_attn_calibrate_mfma(FAKE, 8, 4, 0, sink, None) == 1
+    assert lib.gemma_attn_calibrate_stream(FAKE, 24, 1, sink, None) == 1        # not a multiple of 16
+    assert "multiple of 16" in lib.gemma_attn_last_error().decode()
+    assert lib.gemma_attn_calibrate_stream(FAKE, 32, 1, None, None) == 1
