@@ -93,6 +93,27 @@ def parse():
     return ap.parse_args()
 
 
+def graph_of(fn, torch):
+    """fn captured into a CUDA (HIP) graph after two warm-up calls on a side stream,
+    or None if capture fails.  fn must launch only kernels (no allocation, no sync)."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+    except Exception as e:  # noqa: BLE001
+        print(f"graph capture failed: {e}", file=sys.stderr)
+        return None
+
+
 def timed(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
@@ -469,14 +490,20 @@ def bench_stack_decode(args, torch, api, W):
         step()
     torch.cuda.synchronize()
     sec = timed(step, steps, 0, torch)
+    g = graph_of(step, torch)
+    graph_sec = timed(g.replay, steps, 2, torch) if g is not None else None
+    del g
     nbytes = sum(L["bytes"] for L in layers)
     del layers
     torch.cuda.empty_cache()
     gbs = nbytes / sec / 1e9
     return {
         "workload": "6-layer decode step: 5 local (32q/16kv, d=256, W=1024) + 1 global K=V (32q/4kv, d=512), "
-                    "B=32, context 65536, kv_append then decode per layer",
-        "ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(B / sec, 1), "kv_bytes": nbytes,
+                    "B=32, context 65536, kv_append then decode per layer (graph_ms_per_step: the same step "
+                    "replayed as one HIP graph)",
+        "ms_per_step": round(sec * 1e3, 4),
+        "graph_ms_per_step": None if graph_sec is None else round(graph_sec * 1e3, 4),
+        "tokens_per_s": round(B / sec, 1), "kv_bytes": nbytes,
         "value": round(gbs, 1), "unit": "GB/s", "steps": steps,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / MI355X_HBM_GBS, 4)},
@@ -640,6 +667,9 @@ def bench_stack_verify(args, torch, api, W, q_len=2):
         step()
     torch.cuda.synchronize()
     sec = timed(step, steps, 0, torch)
+    g = graph_of(step, torch)
+    graph_sec = timed(g.replay, steps, 2, torch) if g is not None else None
+    del g
     nbytes = sum(L["bytes"] for L in layers)
     del layers
     torch.cuda.empty_cache()
@@ -647,8 +677,11 @@ def bench_stack_verify(args, torch, api, W, q_len=2):
     return {
         "workload": f"6-layer verification step of {q_len} drafted tokens per sequence: 5 local (32q/16kv, d=256, "
                     f"W=1024, ring of {1024 + q_len - 1} slots) + 1 global K=V (32q/4kv, d=512), B=32, context "
-                    "65536, per layer kv_append of each token then one multi-token decode",
-        "q_len": q_len, "ms_per_step": round(sec * 1e3, 4), "tokens_per_s": round(B * q_len / sec, 1),
+                    "65536, per layer kv_append of each token then one multi-token decode (graph_ms_per_step: replayed "
+                    "as one HIP graph)",
+        "q_len": q_len, "ms_per_step": round(sec * 1e3, 4),
+        "graph_ms_per_step": None if graph_sec is None else round(graph_sec * 1e3, 4),
+        "tokens_per_s": round(B * q_len / sec, 1),
         "kv_bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s", "steps": steps,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / MI355X_HBM_GBS, 4)},
