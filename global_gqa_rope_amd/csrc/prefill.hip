@@ -3,9 +3,11 @@
 // A workgroup owns one KV head of one sequence and QB consecutive query
 // positions: all G query heads of the group at those positions share every key
 // tile it stages in LDS (the grouped-query sharing of "Gemma 4多模态大模型架构详解",
-// section "分组查询注意力").  Its 128 query rows (QB positions x G heads) are
-// split over four waves of 32 rows, one wave per SIMD.  Per key tile of 32
-// positions each wave computes, over the full head dim:
+// section "分组查询注意力").  Its query rows (QB positions x G heads) are
+// split over four waves, one wave per SIMD, each with kRB blocks of 32 rows
+// (one block at d = 512, two at d = 256, so that every key and value
+// fragment read from LDS feeds kRB MFMAs).  Per key tile of 32 positions each
+// wave computes, for each row block, over the full head dim:
 //   S^T[key][row] = K~ Q~^T      32x32x16 bf16 MFMAs, A = key rows read from
 //                                LDS, B = the wave's normalised, rotated queries
 //                                held in registers
@@ -15,8 +17,9 @@
 //   O^T[d][row] += V^T P^T       32x32x16 MFMAs; V^T by transposing LDS reads of
 //                                the value rows, P straight from the score
 //                                registers
-// Each wave keeps 32 rows x d fp32 accumulators (256 registers at d = 512, in
-// the accumulation register file, AGPRs); the scores of a tile stay in VGPRs
+// Each wave keeps 32 kRB rows x d fp32 accumulators (256 registers at d = 512
+// and at d = 256, in the accumulation register file, AGPRs); the scores of a
+// tile stay in VGPRs
 // (MFMAs in VGPR form for QK^T, the PV MFMAs written out with AGPR
 // accumulators).
 //
@@ -49,8 +52,13 @@ template <typename T, int D, int G, bool SHARED>
 struct PrefillCfg {
   static constexpr int KT = kPrepTile;              // keys per tile
   static constexpr int kWaves = 4;
-  static constexpr int kRows = 32;                  // query rows per wave
-  static constexpr int PW = kRows / G;              // positions per wave
+  static constexpr int kRows = 32;                  // query rows of one row block
+  // Row blocks per wave: local (d = 256) bf16 layers take two, so that each
+  // key and value fragment read from LDS feeds two MFMAs and the wave's
+  // 64 x 256 fp32 outputs fill the accumulation registers as the global
+  // layers' 32 x 512 do.
+  static constexpr int kRB = (D == 256 && sizeof(T) == 2) ? 2 : 1;
+  static constexpr int PW = kRB * kRows / G;        // positions per wave
   static constexpr int QB = kWaves * PW;            // positions per workgroup
   static constexpr int kQSteps = D / 16;            // QK^T reduction steps
   static constexpr int kDBlocks = D / 32;           // 32-dim output blocks
@@ -72,8 +80,10 @@ struct PrefillCfg {
   static constexpr int kLdsBytes = kStages * kStageBytes;
   static constexpr int kDmaK = kKBytes / 1024, kDmaV = kVBytes / 1024;
   static constexpr int kDmaPerWave = (kDmaK + kDmaV) / kWaves;
-  static constexpr int kKAhead = 6;                 // key fragment reads in flight
-  static constexpr int kVAhead = 4;                 // value fragments (two reads each) in flight
+  // Key fragment reads in flight (fewer with two row blocks, whose second
+  // query block takes the registers) and value fragments (two reads each).
+  static constexpr int kKAhead = kRB == 2 ? 4 : 6;
+  static constexpr int kVAhead = 4;
   static_assert(kLdsBytes <= kLdsCap, "LDS budget");
   static_assert((kDmaK + kDmaV) % kWaves == 0 && kKBytes % 1024 == 0, "tile copy split");
   static_assert(kKBytes % kVRowBytes == 0 && kStageBytes % kVRowBytes == 0, "row alignment for the swizzle");
@@ -167,21 +177,21 @@ __device__ __forceinline__ float read_acc(float a) {
   return v;
 }
 
-// Scheduling pattern for a pipelined operand stream of N MFMAs, R LDS reads
-// each, whose reads run A MFMAs ahead: the first A*R reads (when PRE; else
-// they were issued before this region), then one MFMA and R reads
-// alternately, then the last A MFMAs; NV global->LDS copies go one after
-// every SV-th MFMA.  Keeps the reads in flight where the scheduler would
+// Scheduling pattern for a pipelined operand stream of N steps of M MFMAs
+// sharing R LDS reads, whose reads run A steps ahead: the first A*R reads
+// (when PRE; else they were issued before this region), then M MFMAs and R
+// reads alternately, then the last A steps; NV global->LDS copies go one
+// after every SV-th step.  Keeps the reads in flight where the scheduler would
 // otherwise trade prefetch depth for registers, and spreads the copies so the
 // wave never queues many of them at once.  Other work (the exponentials) is
 // left to the scheduler: fixed vector-ALU slots between the MFMAs measured
 // slower.
-template <int A, int N, int R, int NV = 0, int SV = 1, bool PRE = true>
+template <int A, int N, int R, int NV = 0, int SV = 1, bool PRE = true, int M = 1>
 __device__ __forceinline__ void interleave_reads_mfma() {
   if constexpr (PRE) __builtin_amdgcn_sched_group_barrier(0x100, A * R, 0);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
     if (i < N - A) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
     if (NV > 0 && i % SV == 0 && i / SV < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
@@ -351,6 +361,19 @@ __device__ __forceinline__ Frag8<T> query_frag(const QSource<T, D>& q, int u, in
   }
 }
 
+// acc + the sum of squares of a bf16 fragment, by paired dot products on the
+// packed values (the squares are exact in fp32).  Working on the packed
+// words also keeps the compiler from holding fp32 copies of the query.
+__device__ __forceinline__ float sum_squares(const Frag8<bf16>& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 p = {f.v[2 * i], f.v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
+}
+
 // Per-lane operand offsets within a stage.
 struct LaneOffsets {
   int kq, vq;      // QK^T key rows: key region, value region (K=V dims >= 128)
@@ -377,22 +400,25 @@ __device__ __forceinline__ void qk_prefetch(Frag8<T> (&kf)[C::kKAhead], const ld
 // after every (kQSteps / NC)-th MFMA, and `work(u)` (other, independent work)
 // after MFMA u in program order.
 template <typename C, typename T, int D, int NC, typename CopyFn, typename WorkFn>
-__device__ __forceinline__ void qk_run(f32x16& s, Frag8<T> (&kf)[C::kKAhead], const lds_char* cur,
-                                       const LaneOffsets& lo, const QSource<T, D>& qs, int h, CopyFn&& copy,
-                                       WorkFn&& work) {
+__device__ __forceinline__ void qk_run(f32x16 (&s)[C::kRB], Frag8<T> (&kf)[C::kKAhead], const lds_char* cur,
+                                       const LaneOffsets& lo, const QSource<T, D> (&qs)[C::kRB], int h,
+                                       CopyFn&& copy, WorkFn&& work) {
   constexpr int kStride = NC > 0 ? C::kQSteps / NC : 1;
-  static_assert(NC <= C::kQSteps, "one copy per QK^T MFMA at most");
-  s = f32x16{};
+  static_assert(NC <= C::kQSteps, "one copy per QK^T step at most");
+#pragma unroll
+  for (int rb = 0; rb < C::kRB; ++rb) s[rb] = f32x16{};
 #pragma unroll
   for (int u = 0; u < C::kQSteps; ++u) {
     const Frag8<T> k = kf[u % C::kKAhead];
     if (u + C::kKAhead < C::kQSteps)
       key_frag(kf[u % C::kKAhead], cur, u + C::kKAhead < C::kKSteps ? lo.kq : lo.vq, u + C::kKAhead);
-    mma32(s, k, query_frag(qs, u, h));
+#pragma unroll
+    for (int rb = 0; rb < C::kRB; ++rb) mma32(s[rb], k, query_frag(qs[rb], u, h));   // one key read, kRB MFMAs
     if (NC > 0 && u % kStride == 0 && u / kStride < NC) copy(u / kStride);
     work(u);
   }
-  if constexpr (sizeof(T) == 2) interleave_reads_mfma<C::kKAhead, C::kQSteps, 1, NC, kStride, false>();
+  if constexpr (sizeof(T) == 2)
+    interleave_reads_mfma<C::kKAhead, C::kQSteps, 1, NC, kStride, false, C::kRB>();
 }
 
 // Scores of an edge tile masked: register r of this lane is key
@@ -452,8 +478,8 @@ __device__ __forceinline__ void tile_exps(Frag8<T> (&pf)[2], const float (&sv)[1
 // O^T += V^T P^T from the value rows of the stage at `st`: step f = 2t + c
 // pairs value block t with keys 16c .. 16c+15 (score registers 8c .. 8c+7).
 template <typename C, typename T, int NB>
-__device__ __forceinline__ void pv_tile(const lds_char* st, const LaneOffsets& lo, const Frag8<T> (&pf)[2],
-                                        RowState<NB>& rs, int lane) {
+__device__ __forceinline__ void pv_tile(const lds_char* st, const LaneOffsets& lo, const Frag8<T> (&pf)[C::kRB][2],
+                                        RowState<NB> (&rs)[C::kRB], int lane) {
   if constexpr (sizeof(T) == 2) {
     Frag8<T> vf[C::kVAhead];
 #pragma unroll
@@ -463,14 +489,16 @@ __device__ __forceinline__ void pv_tile(const lds_char* st, const LaneOffsets& l
       const Frag8<T> v = vf[f % C::kVAhead];
       if (f + C::kVAhead < 2 * C::kDBlocks)
         value_frag<C>(vf[f % C::kVAhead], st + C::kKBytes, lo.vt, (f + C::kVAhead) >> 1, (f + C::kVAhead) & 1);
-      mma32_acc(rs.o[f >> 1], v, pf[f & 1]);
+#pragma unroll
+      for (int rb = 0; rb < C::kRB; ++rb) mma32_acc(rs[rb].o[f >> 1], v, pf[rb][f & 1]);   // one value read
     }
   } else {
 #pragma unroll
     for (int f = 0; f < 2 * C::kDBlocks; ++f) {
       Frag8<T> vf;
       value_frag_f32<C>(vf, st, f >> 1, f & 1, lane);
-      mma32_acc(rs.o[f >> 1], vf, pf[f & 1]);
+#pragma unroll
+      for (int rb = 0; rb < C::kRB; ++rb) mma32_acc(rs[rb].o[f >> 1], vf, pf[rb][f & 1]);
     }
   }
 }
@@ -508,21 +536,24 @@ template <typename C, typename T, int D, bool MASK>
 __device__ __forceinline__ void tile_step(const lds_char* __restrict__ cur, lds_char* __restrict__ nxt,
                                           const char* kbase, const char* vbase, uint32_t kspan, uint32_t vspan,
                                           uint32_t vstride, int next_tile, int wave, int lane, const LaneOffsets& lo,
-                                          const QSource<T, D>& qs, int key0, int pos, int window,
-                                          RowState<C::kDBlocks>& rs) {
+                                          const QSource<T, D> (&qs)[C::kRB], int key0, const int (&pos)[C::kRB],
+                                          int window, RowState<C::kDBlocks> (&rs)[C::kRB]) {
   const int h = lane >> 5;
   const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, vstride, nxt, next_tile, wave, lane);
-  f32x16 s;
+  f32x16 s[C::kRB];
   Frag8<T> kf[C::kKAhead];
   qk_prefetch<C, T, D>(kf, cur, lo);
   qk_run<C, T, D, (C::kStages > 1 ? C::kDmaPerWave : 0)>(s, kf, cur, lo, qs, h, copy, [](int) {});
-  float sv[16];
+  Frag8<T> pf[C::kRB][2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sv[r] = s[r];
-  if constexpr (MASK) mask_scores(sv, key0, pos, window, h);
-  const float m_use = update_max(sv, rs);
-  Frag8<T> pf[2];
-  tile_exps(pf, sv, m_use, rs.l_part);
+  for (int rb = 0; rb < C::kRB; ++rb) {
+    float sv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = s[rb][r];
+    if constexpr (MASK) mask_scores(sv, key0, pos[rb], window, h);
+    const float m_use = update_max(sv, rs[rb]);
+    tile_exps(pf[rb], sv, m_use, rs[rb].l_part);
+  }
   pv_tile<C, T>(cur, lo, pf, rs, lane);
 }
 
@@ -538,29 +569,38 @@ __device__ __forceinline__ void pipe_step(const lds_char* __restrict__ kcur, con
                                           lds_char* __restrict__ nxt, const char* kbase, const char* vbase,
                                           uint32_t kspan, uint32_t vspan, uint32_t vstride, int next_tile, int wave,
                                           int lane,
-                                          const LaneOffsets& lo, const QSource<T, D>& qs, int key0, int pos,
-                                          int window, RowState<C::kDBlocks>& rs, f32x16& s) {
+                                          const LaneOffsets& lo, const QSource<T, D> (&qs)[C::kRB], int key0,
+                                          const int (&pos)[C::kRB], int window, RowState<C::kDBlocks> (&rs)[C::kRB],
+                                          f32x16 (&s)[C::kRB]) {
   const int h = lane >> 5;
   Frag8<T> kf[C::kKAhead];
   if constexpr (NEXT) qk_prefetch<C, T, D>(kf, kcur, lo);
-  float sv[16];
+  float sv[C::kRB][16];
+  float m_use[C::kRB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sv[r] = s[r];
-  if constexpr (MASK) mask_scores(sv, key0, pos, window, h);
-  const float m_use = update_max(sv, rs);
-  Frag8<T> pf[2];
+  for (int rb = 0; rb < C::kRB; ++rb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[rb][r] = s[rb][r];
+    if constexpr (MASK) mask_scores(sv[rb], key0, pos[rb], window, h);
+    m_use[rb] = update_max(sv[rb], rs[rb]);
+  }
+  Frag8<T> pf[C::kRB][2];
   if constexpr (NEXT) {
-    // exponential r after QK^T MFMA r
+    // exponential r of every row block after QK^T step r
     const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, vstride, nxt, next_tile, wave, lane);
     qk_run<C, T, D, C::kDmaPerWave>(s, kf, kcur, lo, qs, h, copy, [&](int u) {
       if (u < 16) {
-        const float p = __builtin_amdgcn_exp2f(sv[u] - m_use);
-        rs.l_part += p;
-        frag_set(pf[u / 8], u % 8, p);
+#pragma unroll
+        for (int rb = 0; rb < C::kRB; ++rb) {
+          const float p = __builtin_amdgcn_exp2f(sv[rb][u] - m_use[rb]);
+          rs[rb].l_part += p;
+          frag_set(pf[rb][u / 8], u % 8, p);
+        }
       }
     });
   } else {
-    tile_exps(pf, sv, m_use, rs.l_part);
+#pragma unroll
+    for (int rb = 0; rb < C::kRB; ++rb) tile_exps(pf[rb], sv[rb], m_use[rb], rs[rb].l_part);
   }
   pv_tile<C, T>(vcur, lo, pf, rs, lane);
 }
@@ -621,11 +661,19 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const int m = lane & 31, h = lane >> 5;                     // row of this lane, half of the slice
   // Query rows are positions q_pos0 .. q_pos0 + seq_len - 1 (q_pos0 > 0: a
   // later chunk of a prompt whose earlier keys are in the workspace rows too).
+  // Row block rb of the wave holds its rows 32 rb .. 32 rb + 31; row r of
+  // the wave is query head r % G at position p0 + wave PW + r / G.  32 is a
+  // multiple of G, so the lane's rows in all blocks share one head.
   const int p0 = a.q_pos0 + qb * C::QB;
-  const int pos = p0 + wave * C::PW + m / G;                  // query position of row m
-  const int lpos = pos - a.q_pos0;                            // its row in q and out
   const int qh = kvh * G + (m % G);                           // query head of row m
-  const bool row_valid = lpos < a.seq_len;
+  int pos[C::kRB], lpos[C::kRB];                              // query position of row m, its row in q and out
+  bool row_valid[C::kRB];
+#pragma unroll
+  for (int rb = 0; rb < C::kRB; ++rb) {
+    pos[rb] = p0 + wave * C::PW + (C::kRows * rb + m) / G;
+    lpos[rb] = pos[rb] - a.q_pos0;
+    row_valid[rb] = lpos[rb] < a.seq_len;
+  }
 
   // ---- tile stream setup (the first kStages - 1 copies start in the prologue) -----
   const int p_last = min(p0 + C::QB, a.q_pos0 + a.seq_len) - 1;
@@ -656,29 +704,39 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   // registers for them, so the fp32 build rebuilds each fragment from the raw
   // query when it is used (a slow path that exists for exact tests).
   constexpr bool kQRegs = sizeof(T) == 2;
-  Frag8<T> qf[kQRegs ? C::kQSteps : 1];
-  const T* __restrict__ qrow = static_cast<const T*>(a.q) +
-      ((static_cast<int64_t>(b) * a.seq_len + (row_valid ? lpos : 0)) * a.n_q_heads + qh) * D;
+  constexpr int kRB = C::kRB;
+  static_assert(kQRegs || kRB == 1, "the fp32 build keeps one row block");
+  Frag8<T> qf[kRB][kQRegs ? C::kQSteps : 1];
+  const T* __restrict__ qrow[kRB];
+  const f32x2* __restrict__ qtable[kRB];
   const T* __restrict__ gq = static_cast<const T*>(a.q_gain);
-  const f32x2* __restrict__ qtable = static_cast<const f32x2*>(a.rope_table) +
-                                     static_cast<int64_t>(row_valid ? pos : 0) * a.n_rot;
-  float rs;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    qrow[rb] = static_cast<const T*>(a.q) +
+               ((static_cast<int64_t>(b) * a.seq_len + (row_valid[rb] ? lpos[rb] : 0)) * a.n_q_heads + qh) * D;
+    qtable[rb] = static_cast<const f32x2*>(a.rope_table) + static_cast<int64_t>(row_valid[rb] ? pos[rb] : 0) * a.n_rot;
+  }
+  float rs[kRB];
   {
-    float ss = 0.f;
+    float ss[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) ss[rb] = 0.f;
     if constexpr (kQRegs) {
       // The query loads go out before the first tiles' copies: loads
       // complete in order, so waiting for the queries does not wait for the
       // copies.
 #pragma unroll
-      for (int u = 0; u < C::kQSteps; ++u) load_frag(qf[u], qrow + 16 * u + 8 * h);
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int u = 0; u < C::kQSteps; ++u) load_frag(qf[rb][u], qrow[rb] + 16 * u + 8 * h);
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < C::kStages - 1; ++i)
         issue_tile<C>(rk, rv, vstride, kt_lo + i, (lds_char*)smem + i * C::kStageBytes, wave, lane);
 #pragma unroll
-      for (int u = 0; u < C::kQSteps; ++u)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss += to_f32(qf[u].v[j]) * to_f32(qf[u].v[j]);
+        for (int u = 0; u < C::kQSteps; ++u) ss[rb] = sum_squares(qf[rb][u], ss[rb]);
     } else {
 #pragma unroll
       for (int i = 0; i < C::kStages - 1; ++i)
@@ -686,15 +744,20 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < C::kQSteps; ++u) {
         Frag8<T> f;
-        load_frag(f, qrow + 16 * u + 8 * h);
+        load_frag(f, qrow[0] + 16 * u + 8 * h);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss += to_f32(f.v[j]) * to_f32(f.v[j]);
+        for (int j = 0; j < 8; ++j) ss[0] += to_f32(f.v[j]) * to_f32(f.v[j]);
       }
     }
-    ss = sum_halves(ss);
-    rs = row_valid ? (1.0f / sqrtf(ss / D + a.eps)) * a.qk_scale_log2 : 0.f;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      ss[rb] = sum_halves(ss[rb]);
+      rs[rb] = row_valid[rb] ? (1.0f / sqrtf(ss[rb] / D + a.eps)) * a.qk_scale_log2 : 0.f;
+    }
   }
-  QSource<T, D> qs{qf, qrow, gq, qtable, rs, a.n_rot};
+  QSource<T, D> qs[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) qs[rb] = QSource<T, D>{qf[rb], qrow[rb], gq, qtable[rb], rs[rb], a.n_rot};
   if constexpr (kQRegs) {
     // Gain and rotation of the register fragments.  The gains and (cos, sin)
     // pairs of kBatch steps are all loaded before any is used, so their round
@@ -707,33 +770,37 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
     for (int u0 = 0; u0 < C::kQSteps; u0 += kBatch) {
       Frag8<T> g[kBatch];
-      f32x2 cs[kBatch][4];
+      f32x2 cs[kRB][kBatch][4];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) load_frag(g[i], gq + 16 * (u0 + i) + 8 * h);
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        if (u0 + i < kRotSteps)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) cs[i][j] = qtable[8 * (u0 + i) + 4 * h + j];
+        for (int i = 0; i < kBatch; ++i)
+          if (u0 + i < kRotSteps)
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int u = u0 + i;
-        float x[8];
+            for (int j = 0; j < 4; ++j) cs[rb][i][j] = qtable[rb][8 * (u0 + i) + 4 * h + j];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = to_f32(qf[u].v[j]) * rs * to_f32(g[i].v[j]);
-        if (u < kRotSteps) {
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float r0 = x[2 * j], r1 = x[2 * j + 1];
-            rotate_pair(r0, r1, cs[i][j]);
-            const bool on = 8 * u + 4 * h + j < a.n_rot;
-            x[2 * j] = on ? r0 : x[2 * j];
-            x[2 * j + 1] = on ? r1 : x[2 * j + 1];
+        for (int i = 0; i < kBatch; ++i) {
+          const int u = u0 + i;
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = to_f32(qf[rb][u].v[j]) * rs[rb] * to_f32(g[i].v[j]);
+          if (u < kRotSteps) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float r0 = x[2 * j], r1 = x[2 * j + 1];
+              rotate_pair(r0, r1, cs[rb][i][j]);
+              const bool on = 8 * u + 4 * h + j < a.n_rot;
+              x[2 * j] = on ? r0 : x[2 * j];
+              x[2 * j + 1] = on ? r1 : x[2 * j + 1];
+            }
           }
-        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) frag_set(qf[u], j, x[j]);
-      }
+          for (int j = 0; j < 8; ++j) frag_set(qf[rb][u], j, x[j]);
+        }
     }
   }
 
@@ -752,11 +819,14 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     }
   }
 
-  RowState<C::kDBlocks> st;
+  RowState<C::kDBlocks> st[kRB];
 #pragma unroll
-  for (int t = 0; t < C::kDBlocks; ++t) st.o[t] = f32x16{};
-  st.m_run = -INFINITY;
-  st.l_part = 0.f;
+  for (int rb = 0; rb < kRB; ++rb) {
+#pragma unroll
+    for (int t = 0; t < C::kDBlocks; ++t) st[rb].o[t] = f32x16{};
+    st[rb].m_run = -INFINITY;
+    st[rb].l_part = 0.f;
+  }
   lds_char* const lds = (lds_char*)smem;
 
   // Edge tiles take the masked step: tiles [kt_lo, lo_end) reach below some
@@ -773,7 +843,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     // tile i + 1.  It reads the keys of tile i + 1 and the values of tile i,
     // and copies tile i + kStages - 1 into the stage of tile i - 1, which
     // every wave has left once it passes the step's barrier.
-    f32x16 s;
+    f32x16 s[kRB];
     {
       wait_tiles<C>(C::kStages - 2);   // tile kt_lo landed; the next kStages - 2 may be in flight
       __builtin_amdgcn_s_barrier();
@@ -841,46 +911,50 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   // ---- epilogue: register r of block t is dim 32t + 8(r/4) + 4h + r%4 of row m -------
   wait_vm_le<0>();   // copies of tiles past the last one have landed before the workgroup ends
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last PV MFMA retired
-  const float l = sum_halves(st.l_part);
-  const float inv = 1.0f / l;
-  T* __restrict__ out = static_cast<T*>(a.out) +
-      ((static_cast<int64_t>(b) * a.seq_len + (row_valid ? lpos : 0)) * a.n_q_heads + qh) * D;
-  if constexpr (sizeof(T) == 2) {
-    // Lanes m and m + 32 hold the two 4-dim halves of each 8-dim run of row
-    // m.  One row swap per pair of runs hands each lane a whole run (lane m
-    // the even run, lane m + 32 the odd one), so every store is 16 bytes.
 #pragma unroll
-    for (int t = 0; t < C::kDBlocks; ++t) {
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float inv = 1.0f / sum_halves(st[rb].l_part);
+    T* __restrict__ out = static_cast<T*>(a.out) +
+        ((static_cast<int64_t>(b) * a.seq_len + (row_valid[rb] ? lpos[rb] : 0)) * a.n_q_heads + qh) * D;
+    if constexpr (sizeof(T) == 2) {
+      // Lanes m and m + 32 hold the two 4-dim halves of each 8-dim run of row
+      // m.  One row swap per pair of runs hands each lane a whole run (lane m
+      // the even run, lane m + 32 the odd one), so every store is 16 bytes.
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint32_t lo[2], hi[2];   // runs 2j (registers 8j..8j+3) and 2j+1 (8j+4..8j+7)
+      for (int t = 0; t < C::kDBlocks; ++t) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          lo[e] = pack_bf16x2(read_acc(st.o[t][8 * j + 2 * e]) * inv, read_acc(st.o[t][8 * j + 2 * e + 1]) * inv);
-          hi[e] = pack_bf16x2(read_acc(st.o[t][8 * j + 4 + 2 * e]) * inv,
-                              read_acc(st.o[t][8 * j + 4 + 2 * e + 1]) * inv);
-          const auto r = __builtin_amdgcn_permlane32_swap(lo[e], hi[e], false, false);
-          lo[e] = r[0];
-          hi[e] = r[1];
+        for (int j = 0; j < 2; ++j) {
+          uint32_t lo[2], hi[2];   // runs 2j (registers 8j..8j+3) and 2j+1 (8j+4..8j+7)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            lo[e] = pack_bf16x2(read_acc(st[rb].o[t][8 * j + 2 * e]) * inv,
+                                read_acc(st[rb].o[t][8 * j + 2 * e + 1]) * inv);
+            hi[e] = pack_bf16x2(read_acc(st[rb].o[t][8 * j + 4 + 2 * e]) * inv,
+                                read_acc(st[rb].o[t][8 * j + 4 + 2 * e + 1]) * inv);
+            const auto r = __builtin_amdgcn_permlane32_swap(lo[e], hi[e], false, false);
+            lo[e] = r[0];
+            hi[e] = r[1];
+          }
+          if (row_valid[rb])
+            *reinterpret_cast<uint4*>(out + 32 * t + 16 * j + 8 * h) = uint4{lo[0], lo[1], hi[0], hi[1]};
         }
-        if (row_valid)
-          *reinterpret_cast<uint4*>(out + 32 * t + 16 * j + 8 * h) = uint4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    } else {
+      // fp32: each 4-dim half is 16 bytes already
+      if (row_valid[rb]) {
+#pragma unroll
+        for (int t = 0; t < C::kDBlocks; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float4 v;
+            v.x = read_acc(st[rb].o[t][4 * q]) * inv;
+            v.y = read_acc(st[rb].o[t][4 * q + 1]) * inv;
+            v.z = read_acc(st[rb].o[t][4 * q + 2]) * inv;
+            v.w = read_acc(st[rb].o[t][4 * q + 3]) * inv;
+            *reinterpret_cast<float4*>(out + 32 * t + 8 * q + 4 * h) = v;
+          }
       }
     }
-  } else {
-    // fp32: each 4-dim half is 16 bytes already
-    if (!row_valid) return;
-#pragma unroll
-    for (int t = 0; t < C::kDBlocks; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float4 v;
-        v.x = read_acc(st.o[t][4 * q]) * inv;
-        v.y = read_acc(st.o[t][4 * q + 1]) * inv;
-        v.z = read_acc(st.o[t][4 * q + 2]) * inv;
-        v.w = read_acc(st.o[t][4 * q + 3]) * inv;
-        *reinterpret_cast<float4*>(out + 32 * t + 8 * q + 4 * h) = v;
-      }
   }
 }
 
