@@ -78,6 +78,7 @@ struct DecodeCfg {
                                 : (2 * kPerWaveBytes + kCommonBytes <= kLdsLimit) ? 2
                                                                                   : 1;
   static constexpr int kDmaPerTile = kTileBytes / 1024;
+  static constexpr int kQ8Copies = kCodeBytes / 1024 + 1;   // Q8: copy instructions of one tile
   static constexpr int kKDma = kKBytes / 1024;
   // LDS map: [wave][buf] tiles | [wave][2] staging (Q8) | [wave] coarse angles |
   // query operand | fine angles | misc
@@ -200,17 +201,20 @@ template <typename C>
 __device__ __forceinline__ void expand_q8(const lds_char* __restrict__ stage, lds_char* __restrict__ tile, int lane) {
   constexpr int kD = C::kD;
   static_assert(kD == 64 * 8, "one 8-code piece per lane and row");
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  // all the tile's code reads first, so their latencies overlap
+  u32x2 w[C::KT];
+#pragma unroll
+  for (int r = 0; r < C::KT; ++r) w[r] = *(const __attribute__((address_space(3))) u32x2*)(stage + r * kD + 8 * lane);
 #pragma unroll
   for (int r = 0; r < C::KT; ++r) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(stage + r * kD + 8 * lane);
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 packed;
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {   // sign-extend and convert each byte, pack pairs
-      const f32x2 x{static_cast<float>(static_cast<int8_t>(w[j / 4] >> (8 * (j % 4)))),
-                    static_cast<float>(static_cast<int8_t>(w[j / 4] >> (8 * (j % 4 + 1))))};
+      const f32x2 x{static_cast<float>(static_cast<int8_t>(w[r][j / 4] >> (8 * (j % 4)))),
+                    static_cast<float>(static_cast<int8_t>(w[r][j / 4] >> (8 * (j % 4 + 1))))};
       packed[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
     }
     const bf16x8 v = __builtin_bit_cast(bf16x8, packed);
@@ -481,6 +485,10 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
     }
   };
   issue(Q8 ? stage_buf : tile_buf, 0);
+  // Q8: the tile after it too; the staging buffer of tile k is refilled with
+  // tile k + 2 as soon as tile k is expanded, so two copies are in flight
+  // while a tile is computed (a tile's codes are half the bytes of a bf16 tile).
+  if constexpr (Q8) issue(stage_buf + C::kStageBytes, 1);
 
   // ---- rotation rates of the lane's pairs lane + 64 m (fp64, one exp2 each) ------
   constexpr int kPairsPerLane = D / 128;
@@ -610,22 +618,33 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
       if (g >= p_end) break;
       const int key0 = (g - cur.T) * C::KT;
       const uint32_t buf = Q8 ? 0u : (k & 1) * C::kTileBytes;
-      wait_vm_le<0>();   // tile k has landed: it is the wave's only copy in flight
+      if constexpr (Q8) {
+        // tile k has landed once at most the copy of tile k + 1 (if there is
+        // one) is in flight
+        if (g + C::kWaves < t_end) wait_vm_le<C::kQ8Copies>();
+        else wait_vm_le<0>();
+      } else {
+        wait_vm_le<0>();   // tile k has landed: it is the wave's only copy in flight
+      }
       // The step runs in a function whose buffers are restrict pointers: the
       // compiler then knows the copy of tile k + 1 into `nxt` does not feed
       // the reads of `cur_buf` (or of `stage`), and adds no wait for it before
       // them.
       auto step = [&](lds_char* __restrict__ cur_buf, lds_char* __restrict__ nxt,
-                      const lds_char* __restrict__ stage) {
+                      lds_char* __restrict__ stage) {
         u32x4 head_cur[C::kHeadSteps > 0 ? C::kHeadSteps : 1];   // PRE: tile k's heads (landed with it)
         if constexpr (PRE) {
   #pragma unroll
           for (int u = 0; u < C::kHeadSteps; ++u) head_cur[u] = head_next[u];
         }
-        issue(nxt, k + 1);
+        f32x4 row_scale;   // Q8: scales of the lane's keys 4 kg .. 4 kg + 3
         if constexpr (Q8) {
           expand_q8<C>(stage, cur_buf, lane);
-          asm volatile("" ::: "memory");   // the tile's writes come before its operand reads
+          row_scale = *(const __attribute__((address_space(3))) f32x4*)(stage + C::kCodeBytes + 16 * kg);
+          lds_fence();   // the codes and scales are read before tile k + 2 lands on them
+          issue(stage, k + 2);
+        } else {
+          issue(nxt, k + 1);
         }
 
         // S^T = K~ Q~^T; the lane's A operand is key row hcol, dims 32u + 8kg .. +7.
@@ -647,11 +666,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
           __builtin_amdgcn_sched_barrier(0);
         }
         f32x4 s = sa + sb;
-        f32x4 row_scale;   // Q8: scales of the lane's keys 4 kg .. 4 kg + 3
-        if constexpr (Q8) {
-          row_scale = *(const __attribute__((address_space(3))) f32x4*)(stage + C::kCodeBytes + 16 * kg);
-          s *= row_scale;
-        }
+        if constexpr (Q8) s *= row_scale;
         if constexpr (C::kRot > 0) {   // publish the wave's next tile's coarse angles
           if ((k + 1) % kAnchor == 0) {
             coarse_l = rope_cos_sin(static_cast<double>(key0 + C::kWaves * C::KT) * w_pair[0]);
