@@ -36,20 +36,20 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 # still match; after any change to them the figure is stale and reads null.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                     "bytes": 7829884936},
-    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                           "bytes": 8595751022},
-    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "1ee53259defdc92b",
-                           "bytes": 1570822828},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "ddb3242cba379522",
-                      "bytes": 4288878449},
-    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "ddb3242cba379522",
-                            "bytes": 4312480994},
-    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "ddb3242cba379522",
-                                 "bytes": 5355113227},
-    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "ddb3242cba379522",
-                           "bytes": 2173367760},
+    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "2315a3c08e0171da",
+                     "bytes": 7862809472},
+    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "2315a3c08e0171da",
+                           "bytes": 10619417690},
+    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "2315a3c08e0171da",
+                           "bytes": 1583837990},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "6fc2be6d049b6f4b",
+                      "bytes": 4288872720},
+    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "6fc2be6d049b6f4b",
+                            "bytes": 4312478888},
+    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "6fc2be6d049b6f4b",
+                                 "bytes": 5355004224},
+    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "6fc2be6d049b6f4b",
+                           "bytes": 2173368972},
 }
 
 
@@ -90,7 +90,18 @@ def parse():
                     help="skip the measured-peak probes (an MFMA chain on random bf16 operands, a streaming read)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
-    return ap.parse_args()
+    ap.add_argument("--only", default=None,
+                    help="comma list of legs to run after the global prefill (decode, multi, prerotated, int8, "
+                         "chunk, local, stack, verify); the others are skipped (for per-leg profiles)")
+    args = ap.parse_args()
+    if args.only is not None:
+        legs = {x for x in args.only.split(",") if x}
+        known = {"decode", "multi", "prerotated", "int8", "chunk", "local", "stack", "verify"}
+        if not legs <= known:
+            ap.error(f"--only: unknown legs {sorted(legs - known)}")
+        for leg in known - legs:
+            setattr(args, "no_" + leg, True)
+    return args
 
 
 def graph_of(fn, torch):
