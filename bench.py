@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--no-int8", action="store_true", help="skip the int8-cache decode leg")
     ap.add_argument("--no-prerotated", action="store_true", help="skip the pre-rotated-cache decode leg")
     ap.add_argument("--no-chunk", action="store_true", help="skip the chunked prefill leg")
+    ap.add_argument("--no-long", action="store_true", help="skip the 256K-context decode leg")
+    ap.add_argument("--no-estack", action="store_true",
+                    help="skip the 4:1 stack decode leg of the smaller models' layer types")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-calibrate", action="store_true",
                     help="skip the measured-peak probes (an MFMA chain on random bf16 operands, a streaming read)")
@@ -92,11 +95,12 @@ def parse():
                     help="first run a plain 256 MiB device copy, the reference for HBM byte counters")
     ap.add_argument("--only", default=None,
                     help="comma list of legs to run after the global prefill (decode, multi, prerotated, int8, "
-                         "chunk, local, stack, verify); the others are skipped (for per-leg profiles)")
+                         "chunk, local, stack, verify, long, estack); the others are skipped (for per-leg "
+                         "profiles)")
     args = ap.parse_args()
     if args.only is not None:
         legs = {x for x in args.only.split(",") if x}
-        known = {"decode", "multi", "prerotated", "int8", "chunk", "local", "stack", "verify"}
+        known = {"decode", "multi", "prerotated", "int8", "chunk", "local", "stack", "verify", "long", "estack"}
         if not legs <= known:
             ap.error(f"--only: unknown legs {sorted(legs - known)}")
         for leg in known - legs:
@@ -215,6 +219,49 @@ def bench_decode(args, torch, api, W):
     return {"sec": sec, "bytes": nbytes, "split_ms": split_ms / max(n_split, 1),
             "merge_ms": merge_ms / max(n_merge, 1), "append_ms": append_ms / max(n_append, 1), "lens": lens,
             "cpu": cpu}
+
+
+def bench_long_decode(args, torch, api, W):
+    """Global K=V decode at the pages' longest context: B=4, every sequence at 262144 keys."""
+    wl = W.CONFIGS["long_decode"]
+    shape = wl.layer
+    dev = torch.device("cuda", 0)
+    lens = wl.lengths()
+    B, cap, D = wl.batch, wl.cache_cap(), shape.head_dim
+    kc = W.normal((B, shape.n_kv_heads, cap, D), wl.seed, "k_cache", torch.bfloat16, dev)
+    q = W.normal((B, shape.n_q_heads, D), wl.seed, "q_dec", torch.bfloat16, dev)
+    g_q = W.gains(D, wl.seed, "g_q", False, torch.bfloat16, dev)
+    lay = api.Layer.from_shape(shape, torch.bfloat16)
+    seq = lens.to(dev)
+    maxlen = int(lens.max())
+    out = torch.empty_like(q)
+    ws = api.workspace(api.gemma_attn_decode_workspace_size(lay, B, maxlen), dev)
+
+    def step():
+        api.gemma_attn_decode(lay, q, g_q, kc, None, seq, maxlen, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    sec = timed(step, args.decode_steps, 0, torch)
+    api.profile_enable(False)
+    split_ms, n_split = api.profile_read("decode_splitk")
+    api.profile_reset()
+    nbytes = wl.kv_bytes(lens)
+    del kc
+    torch.cuda.empty_cache()
+    split_ms /= max(n_split, 1)
+    return {
+        "workload": "global K=V layer decode at 256K context: B=4, 262144 cached keys per sequence, 32q/4kv, d=512",
+        "value": round(nbytes / sec / 1e9, 1), "unit": "GB/s", "ms_per_step": round(sec * 1e3, 4),
+        "tokens_per_s": round(B / sec, 1), "kv_bytes": nbytes,
+        "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V>", "bound": "hbm",
+                     "achieved": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
+                     "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4), "traffic": None,
+                     "avg_ms": round(split_ms, 4)},
+    }
 
 
 def bench_local_prefill(args, torch, api, W):
@@ -463,13 +510,15 @@ def bench_prerotated_decode(args, torch, api, W):
     }
 
 
-def bench_stack_decode(args, torch, api, W):
-    """One decode step of a 6-layer stack (5 local + 1 global), each layer kv_append then decode."""
-    wl_l, wl_g = W.CONFIGS["stack_decode_local"], W.CONFIGS["stack_decode_global"]
+def bench_stack_decode(args, torch, api, W, local="stack_decode_local", glob="stack_decode_global", n_local=5,
+                       workload=None):
+    """One decode step of a stack of n_local local layers and one global layer, each layer kv_append then
+    decode."""
+    wl_l, wl_g = W.CONFIGS[local], W.CONFIGS[glob]
     dev = torch.device("cuda", 0)
     B = wl_l.batch
     layers = []
-    for i, wl in enumerate([wl_l] * 5 + [wl_g]):
+    for i, wl in enumerate([wl_l] * n_local + [wl_g]):
         shape = wl.layer
         D, Hkv = shape.head_dim, shape.n_kv_heads
         seed = wl.seed + i
@@ -509,9 +558,9 @@ def bench_stack_decode(args, torch, api, W):
     torch.cuda.empty_cache()
     gbs = nbytes / sec / 1e9
     return {
-        "workload": "6-layer decode step: 5 local (32q/16kv, d=256, W=1024) + 1 global K=V (32q/4kv, d=512), "
-                    "B=32, context 65536, kv_append then decode per layer (graph_ms_per_step: the same step "
-                    "replayed as one HIP graph)",
+        "workload": workload or ("6-layer decode step: 5 local (32q/16kv, d=256, W=1024) + 1 global K=V (32q/4kv, "
+                                 "d=512), B=32, context 65536, kv_append then decode per layer (graph_ms_per_step: "
+                                 "the same step replayed as one HIP graph)"),
         "ms_per_step": round(sec * 1e3, 4),
         "graph_ms_per_step": None if graph_sec is None else round(graph_sec * 1e3, 4),
         "tokens_per_s": round(B / sec, 1), "kv_bytes": nbytes,
@@ -808,6 +857,14 @@ def main():
         line["stack_decode"] = bench_stack_decode(args, torch, api, W)
     if not args.no_verify:
         line["stack_verify"] = bench_stack_verify(args, torch, api, W)
+    if not args.no_long:
+        line["long_decode"] = bench_long_decode(args, torch, api, W)
+    if not args.no_estack:
+        line["e_stack_decode"] = bench_stack_decode(
+            args, torch, api, W, "e_stack_local", "e_stack_global", 4,
+            "5-layer decode step of the smaller models' layer types, 4:1: 4 local (8q/2kv, d=256, W=512) + 1 global "
+            "with a separate V cache (8q/2kv, d=512, keys stored rotated), B=32, context 65536, kv_append then "
+            "decode per layer (graph_ms_per_step: the same step replayed as one HIP graph)")
     if not args.no_calibrate:
         cal = calibrate(torch, api)
         line["calibration"] = cal

@@ -179,6 +179,12 @@ CONFIGS = {
                                          65536, torch.bfloat16),
     "stack_decode_global": DecodeWorkload("stack_decode_global", GLOBAL_LAYER, 32, 65536,
                                           65536, torch.bfloat16),
+    # the longest context the pages give (256K): every sequence at 262144 keys
+    "long_decode": DecodeWorkload("long_decode", GLOBAL_LAYER, 4, 262143, 262143, torch.bfloat16),
+    # a 4:1 stack of the smaller models' layer types (512-token windows, a
+    # global layer with a separate V cache)
+    "e_stack_local": DecodeWorkload("e_stack_local", E_LOCAL_LAYER, 32, 65536, 65536, torch.bfloat16),
+    "e_stack_global": DecodeWorkload("e_stack_global", E_GLOBAL_LAYER, 32, 65536, 65536, torch.bfloat16),
 }
 
 TINY_DECODE_STEPS = 16
