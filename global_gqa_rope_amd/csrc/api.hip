@@ -1,6 +1,7 @@
 // C ABI: argument validation, workspace layout and kernel dispatch.
 // Validation runs entirely on the host before any HIP call, so every error
 // path is exercised without a GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -64,6 +65,10 @@ struct ProfScope {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+// Query columns (token x head of the group) of one decode launch, and of one
+// call (as several launches).
+constexpr int kDecodeColumns = 16;
+constexpr int kDecodeMaxColumns = 64;
 
 struct Derived {
   int group;
@@ -209,10 +214,15 @@ int decode_tiles_per_seq(const ga_layer* L, int max_seq_len, int cache_cap) {
 // depend on the device; the launch then uses one workgroup per CU at most.
 constexpr int kMaxDecodeCUs = 1 << 20;
 
+// The query tokens of one decode launch fill the 16 columns of its QK^T MFMAs
+// (G heads per token); more tokens take several launches over the cache.
+int decode_pass_tokens(const Derived& dv, int q_len) { return std::min(q_len, kDecodeColumns / dv.group); }
+
 bool decode_plan(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len, int cache_cap,
                  int n_cus, ga::DecodePlan* plan) {
   return ga::plan_decode(L->dtype, L->head_dim, dv.group, L->kv_shared, batch, L->n_kv_heads,
-                         decode_tiles_per_seq(L, max_seq_len, cache_cap), n_cus, q_len, plan);
+                         decode_tiles_per_seq(L, max_seq_len, cache_cap), n_cus, decode_pass_tokens(dv, q_len),
+                         plan);
 }
 
 size_t decode_bytes(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len) {
@@ -221,13 +231,14 @@ size_t decode_bytes(const ga_layer* L, const Derived& dv, int batch, int q_len, 
   return align_up(plan.bytes());
 }
 
-// The query tokens of one decode call fill the 16 columns of the QK^T MFMA:
-// q_len tokens x G heads must fit.
+// Query tokens of one decode call: q_len tokens x G heads, at most
+// kDecodeMaxColumns (launched kDecodeColumns at a time).
 ga_status check_q_len(const ga_layer* L, const Derived& dv, int q_len) {
   (void)L;
   if (q_len < 1) return fail(GA_EINVAL, "q_len must be >= 1");
-  if (q_len * dv.group > 16)
-    return fail(GA_EUNSUPPORTED, "q_len %d x %d query heads per KV head exceeds 16 query columns", q_len, dv.group);
+  if (q_len * dv.group > kDecodeMaxColumns)
+    return fail(GA_EUNSUPPORTED, "q_len %d x %d query heads per KV head exceeds %d query columns (%d passes of %d)",
+                q_len, dv.group, kDecodeMaxColumns, kDecodeMaxColumns / kDecodeColumns, kDecodeColumns);
   return GA_OK;
 }
 
@@ -361,9 +372,18 @@ ga_status decode_impl(const ga_layer* layer, int32_t batch, int32_t q_len, const
   da.k_scales = q8_scales(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
   da.k_heads = pre_heads(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
   da.eps = layer->norm_eps; da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
-  return hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
+  // One launch (split-K and merge) per 16 query columns; the launches reuse
+  // the scratch in stream order.
+  const int per = decode_pass_tokens(dv, q_len);
+  for (int tok0 = 0; tok0 < q_len; tok0 += per) {
+    da.tok0 = tok0;
+    da.n_tok = std::min(per, q_len - tok0);
+    st = hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
                                       static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),
                     "decode launch");
+    if (st != GA_OK) return st;
+  }
+  return GA_OK;
 }
 
 }  // namespace

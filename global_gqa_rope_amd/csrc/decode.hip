@@ -391,7 +391,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
   using C = DecodeCfg<T, D, G, SHARED, Q8, PRE>;
   static_assert(C::KT == kDecodeTile, "tile size");
   const int kSlot = a.slot_floats;
-  const int ncol = G * a.q_len;   // query columns: column c is token c / G, head c % G (<= 16)
+  const int ncol = G * a.n_tok;   // query columns: column c is token tok0 + c / G, head c % G (<= 16)
   __shared__ __attribute__((aligned(4096))) char smem[C::kLdsBytes];
 
   const int wg = blockIdx.x, P = gridDim.x;
@@ -538,13 +538,13 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
 
     // ---- query prep: QKNorm + rotation at each token's position, written in
     // operand order.  Operand fragment u, lane hcol + 16 kg, element j =
-    // q~[hcol][32u + 8kg + j]; column c is token c / G (position
-    // L - q_len + c / G) and head c % G of the group; columns >= G q_len are
-    // zeros.  One wave per column: lane owns pairs lane + 64 m.
+    // q~[hcol][32u + 8kg + j]; column c is token tok0 + c / G (position
+    // L - q_len + tok0 + c / G) and head c % G of the group; columns >= G n_tok
+    // are zeros.  One wave per column: lane owns pairs lane + 64 m.
     {
       const int L = a.seq_lens[cur.b];
       for (int h = wave; h < 16; h += C::kWaves) {
-        const int tok = h / G;
+        const int tok = a.tok0 + h / G;
         const T* __restrict__ q = static_cast<const T*>(a.q) +
             ((static_cast<int64_t>(cur.b) * a.q_len + (h < ncol ? tok : 0)) * a.n_q_heads + cur.kvh * G + h % G) * D;
         float x[kPairsPerLane][2];
@@ -607,9 +607,9 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
     // key_lim = P + 1.  Windowed layers: slot s of the ring holds position
     // base + s, or base + s - cache_cap past the newest slot h = (L - 1) mod
     // cache_cap, and is seen when P - W < position <= P.
-    const int key_lim = cur.keys - ((hcol < ncol) ? a.q_len - 1 - hcol / G : 0);
+    const int key_lim = cur.keys - ((hcol < ncol) ? a.q_len - 1 - (a.tok0 + hcol / G) : 0);
     const int L_cur = a.seq_lens[cur.b];
-    const int col_pos = L_cur - a.q_len + ((hcol < ncol) ? hcol / G : a.q_len - 1);
+    const int col_pos = L_cur - a.q_len + ((hcol < ncol) ? a.tok0 + hcol / G : a.q_len - 1);
     const int ring_h = a.window > 0 ? (L_cur - 1) % a.cache_cap : 0;
     const int ring_base = L_cur - 1 - ring_h;
 
@@ -760,14 +760,14 @@ template <typename T, int D, int G, bool SHARED>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, G, SHARED>;
   const int kSlot = a.slot_floats;
-  const int ncol = G * a.q_len;
+  const int ncol = G * a.n_tok;
   __shared__ float wgt[1024];
   __shared__ float red[256];
-  const int seg = blockIdx.x / ncol, h = blockIdx.x % ncol;   // h: column (token h / G, head h % G)
+  const int seg = blockIdx.x / ncol, h = blockIdx.x % ncol;   // h: column (token tok0 + h / G, head h % G)
   const int b = seg / a.n_kv_heads, kvh = seg % a.n_kv_heads;
   const int t = threadIdx.x;
   T* __restrict__ out = static_cast<T*>(a.out) +
-      ((static_cast<int64_t>(b) * a.q_len + h / G) * a.n_q_heads + kvh * G + h % G) * D;
+      ((static_cast<int64_t>(b) * a.q_len + a.tok0 + h / G) * a.n_q_heads + kvh * G + h % G) * D;
   const int keys = decode_keys(a, b);
   if (keys < 0) {
     for (int d = t; d < D; d += 256) out[d] = from_f32<T>(NAN);
@@ -849,7 +849,7 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t s, LaunchTimer tim
   if (timer) timer(s, 2, false);
   if (e != hipSuccess) return e;
   if (timer) timer(s, 3, true);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, G, SHARED>), dim3(a.batch * a.n_kv_heads * G * a.q_len), dim3(256),
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, G, SHARED>), dim3(a.batch * a.n_kv_heads * G * a.n_tok), dim3(256),
                      0, s, a);
   e = hipGetLastError();
   if (timer) timer(s, 3, false);

@@ -81,6 +81,7 @@ struct DecodeArgs {
   float* partials;         // [slots][slot_floats] fp32: o per column, then (m, l) per column
   int batch, n_q_heads, n_kv_heads, n_rot, window, cache_cap, max_seq_len;
   int q_len;               // query tokens per sequence: the last q_len positions (1 = one token)
+  int tok0, n_tok;         // this launch's tokens tok0 .. tok0 + n_tok - 1 (G n_tok <= 16 query columns)
   const float* k_scales;   // int8 K=V cache: per-row scales [B][Hkv][cache_cap] (else null)
   const void* k_heads;     // pre-rotated K=V cache: heads [B][Hkv][cache_cap][2 n_rot] (else null)
   int slot_floats;         // q_len * G * D + 64

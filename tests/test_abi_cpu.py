@@ -125,12 +125,14 @@ def test_multi_token_decode_validation(lib):
         ctypes.byref(kw.get("layer", g)), 2, kw.get("T", 2), FAKE, FAKE, FAKE, kw.get("v", None),
         kw.get("cap", 4096), FAKE, 4096, FAKE, FAKE, 1 << 40, None)
     assert dec(T=0) == 1                                        # q_len >= 1
-    assert dec(T=3) == 2                                        # 3 tokens x 8 heads > 16 columns
-    assert "16 query columns" in lib.gemma_attn_last_error().decode()
+    assert dec(T=9) == 2                                        # 9 tokens x 8 heads > 64 columns
+    assert "64 query columns" in lib.gemma_attn_last_error().decode()
     assert dec(layer=loc, T=2, v=FAKE, cap=1024) == 1           # a W-slot ring is too small for 2 tokens
     assert "1025 slots" in lib.gemma_attn_last_error().decode()
     wsz = lambda layer, B, T, n: lib.gemma_attn_decode_multi_workspace_size(ctypes.byref(layer), B, T, n)
-    assert wsz(g, 2, 0, 4096) == 0 and wsz(g, 2, 3, 4096) == 0
+    assert wsz(g, 2, 0, 4096) == 0 and wsz(g, 2, 9, 4096) == 0
+    # past 16 columns the call runs one pass per 16 columns, each with a 16-column plan
+    assert wsz(g, 2, 3, 4096) == wsz(g, 2, 4, 4096) == decode_ws(2, 4, 16, 512, 4096)
     assert wsz(loc, 2, 2, 4096) == decode_ws(2, 16, 4, 256, 4096)     # 2 tokens x G = 2 columns per slot
     # one token is the single-token call; two tokens widen every slot to 2 G d outputs
     assert wsz(g, 2, 1, 4096) == lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 4096)

@@ -43,6 +43,8 @@ def _caches(shape, B, cap, dev):
     ("e_local", 515, 3, 0),      # slots wrap within the three new tokens (ring of 514 slots)
     ("e_global", 1500, 4, 0),    # separate-V global layer, slot = position
     ("e_global", 40, 2, 0),
+    ("local", 2100, 11, 0),      # 22 columns: two passes over the ring (8 + 3 tokens)
+    ("e_global", 900, 7, 0),     # G = 4: 28 columns, two passes (4 + 3 tokens)
 ])
 def test_multi_token_decode_every_layer_type(kind, S, T, extra):
     shape = SHAPES[kind]

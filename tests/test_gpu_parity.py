@@ -226,6 +226,9 @@ def _multi_case(shape, lens, T, seed, dtype=torch.bfloat16):
     (16, 3, [3, 40, 1500]),                  # G = 4: 12 columns, 4 padding
     (8, 8, [8, 33, 700, 2049]),              # G = 2: 16 columns
     (32, 1, [1, 100, 3000]),                 # one token through the multi-token call
+    (32, 3, [3, 20, 1030, 2600]),            # G = 8: 24 columns, two passes (2 + 1 tokens)
+    (32, 4, [4, 17, 1025, 4100]),            # G = 8: 32 columns, two passes (a 4-token draft)
+    (32, 8, [8, 900, 2049]),                 # G = 8: 64 columns, four passes
 ])
 def test_multi_token_decode_bf16(hq, T, lens):
     shape = W.replace(W.GLOBAL_LAYER, n_q_heads=hq)
