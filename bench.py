@@ -391,8 +391,8 @@ def bench_multi_decode(args, torch, api, W, q_len=2):
         "roofline": {"kernel": "decode_kernel<bf16,512,8,K=V>", "bound": "hbm",
                      "achieved": round(nbytes / (split_ms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS, "unit": "GB/s",
                      "frac": round(nbytes / (split_ms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4),
-                     "traffic": measured_traffic("multi_decode_splitk"),
-                     "avg_ms": round(split_ms, 4)},
+                     "traffic": measured_traffic("multi_decode_splitk") if q_len == 2 else None,
+                     "avg_ms": round(split_ms, 4), "launches_per_call": round(n_split / max(args.decode_steps, 1), 2)},
     }
 
 
@@ -839,6 +839,8 @@ def main():
         cpu_dec = dec["cpu"]
     if not args.no_multi:
         line["multi_token_decode"] = bench_multi_decode(args, torch, api, W)
+        # a 4-token draft on the G = 8 layer: 32 query columns, two column groups in one launch
+        line["multi_token_decode_4"] = bench_multi_decode(args, torch, api, W, q_len=4)
     if not args.no_prerotated:
         line["prerotated_decode"] = bench_prerotated_decode(args, torch, api, W)
         if "decode" in line:

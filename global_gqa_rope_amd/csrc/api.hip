@@ -65,9 +65,10 @@ struct ProfScope {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-// Query columns (token x head of the group) of one decode launch, and of one
-// call (as several launches).
+// Query columns (token x head of the group) of one column group, of one decode
+// launch (two groups), and of one call (as several launches).
 constexpr int kDecodeColumns = 16;
+constexpr int kDecodeLaunchColumns = 32;
 constexpr int kDecodeMaxColumns = 64;
 
 struct Derived {
@@ -214,25 +215,35 @@ int decode_tiles_per_seq(const ga_layer* L, int max_seq_len, int cache_cap) {
 // depend on the device; the launch then uses one workgroup per CU at most.
 constexpr int kMaxDecodeCUs = 1 << 20;
 
-// The query tokens of one decode launch fill the 16 columns of its QK^T MFMAs
-// (G heads per token); more tokens take several launches over the cache.
-int decode_pass_tokens(const Derived& dv, int q_len) { return std::min(q_len, kDecodeColumns / dv.group); }
+// The query tokens of one column group fill the 16 columns of its QK^T MFMAs
+// (G heads per token).  A launch takes one group, or two for 17..32 columns
+// (both streaming the same tiles); more tokens take several launches.
+int decode_pass_tokens(const Derived& dv, int q_len) { return std::min(q_len, kDecodeLaunchColumns / dv.group); }
+int decode_groups(const Derived& dv, int n_tok) { return n_tok * dv.group > kDecodeColumns ? 2 : 1; }
 
-bool decode_plan(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len, int cache_cap,
+bool decode_plan(const ga_layer* L, const Derived& dv, int batch, int n_tok, int max_seq_len, int cache_cap,
                  int n_cus, ga::DecodePlan* plan) {
   return ga::plan_decode(L->dtype, L->head_dim, dv.group, L->kv_shared, batch, L->n_kv_heads,
-                         decode_tiles_per_seq(L, max_seq_len, cache_cap), n_cus, decode_pass_tokens(dv, q_len),
+                         decode_tiles_per_seq(L, max_seq_len, cache_cap), n_cus, n_tok, decode_groups(dv, n_tok),
                          plan);
 }
 
+// Scratch of a call: the largest of its launches' plans (a full launch, and
+// a last one with fewer tokens).
 size_t decode_bytes(const ga_layer* L, const Derived& dv, int batch, int q_len, int max_seq_len) {
-  ga::DecodePlan plan;
-  if (!decode_plan(L, dv, batch, q_len, max_seq_len, 0, kMaxDecodeCUs, &plan)) return 0;
-  return align_up(plan.bytes());
+  const int per = decode_pass_tokens(dv, q_len);
+  size_t need = 0;
+  for (int n : {per, q_len % per}) {
+    if (n == 0) continue;
+    ga::DecodePlan plan;
+    if (!decode_plan(L, dv, batch, n, max_seq_len, 0, kMaxDecodeCUs, &plan)) return 0;
+    need = std::max(need, plan.bytes());
+  }
+  return align_up(need);
 }
 
 // Query tokens of one decode call: q_len tokens x G heads, at most
-// kDecodeMaxColumns (launched kDecodeColumns at a time).
+// kDecodeMaxColumns (launched kDecodeLaunchColumns at a time).
 ga_status check_q_len(const ga_layer* L, const Derived& dv, int q_len) {
   (void)L;
   if (q_len < 1) return fail(GA_EINVAL, "q_len must be >= 1");
@@ -350,13 +361,16 @@ ga_status decode_impl(const ga_layer* layer, int32_t batch, int32_t q_len, const
   hipError_t he = hipGetDevice(&dev);
   if (he == hipSuccess) he = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (he != hipSuccess) return hip_status(he, "decode: device query");
-  ga::DecodePlan plan;
-  if (!decode_plan(layer, dv, batch, q_len, max_seq_len, cache_cap, cus, &plan))
+  const int per = decode_pass_tokens(dv, q_len);
+  ga::DecodePlan plan, last;   // a full launch, and the last one when it has fewer tokens
+  if (!decode_plan(layer, dv, batch, per, max_seq_len, cache_cap, cus, &plan) ||
+      !decode_plan(layer, dv, batch, q_len % per ? q_len % per : per, max_seq_len, cache_cap, cus, &last))
     return fail(GA_EUNSUPPORTED, "no decode kernel for this layer configuration");
   if (noalloc) {
-    if (plan.bytes() > kNoAllocScratchBytes)
+    const size_t need = std::max(plan.bytes(), last.bytes());
+    if (need > kNoAllocScratchBytes)
       return fail(GA_EWORKSPACE, "decode needs %zu bytes of scratch for batch %d, max_seq_len %d; the static "
-                  "scratch holds %zu (use gemma_attn_decode with a workspace)", plan.bytes(), batch, max_seq_len,
+                  "scratch holds %zu (use gemma_attn_decode with a workspace)", need, batch, max_seq_len,
                   kNoAllocScratchBytes);
     st = device_scratch(dev, static_cast<hipStream_t>(stream), &workspace);
     if (st != GA_OK) return st;
@@ -367,17 +381,21 @@ ga_status decode_impl(const ga_layer* layer, int32_t batch, int32_t q_len, const
   da.tile_prefix = static_cast<int32_t*>(workspace);
   da.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.prefix_bytes);
   da.batch = batch; da.n_q_heads = layer->n_q_heads; da.n_kv_heads = layer->n_kv_heads; da.n_rot = dv.n_rot;
-  da.window = layer->window; da.cache_cap = cache_cap; da.max_seq_len = max_seq_len; da.n_wgs = plan.n_wgs;
-  da.q_len = q_len; da.slot_floats = static_cast<int>(plan.slot_floats);
+  da.window = layer->window; da.cache_cap = cache_cap; da.max_seq_len = max_seq_len;
+  da.q_len = q_len;
   da.k_scales = q8_scales(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
   da.k_heads = pre_heads(layer, dv, const_cast<void*>(k_cache), batch, cache_cap);
   da.eps = layer->norm_eps; da.qk_scale_log2 = dv.scale * 1.4426950408889634f; da.log2_theta = dv.log2_theta;
-  // One launch (split-K and merge) per 16 query columns; the launches reuse
+  // One launch (split-K and merge) per 32 query columns; the launches reuse
   // the scratch in stream order.
-  const int per = decode_pass_tokens(dv, q_len);
   for (int tok0 = 0; tok0 < q_len; tok0 += per) {
     da.tok0 = tok0;
     da.n_tok = std::min(per, q_len - tok0);
+    const ga::DecodePlan& pl = da.n_tok == per ? plan : last;
+    da.n_wgs = pl.n_wgs;
+    da.n_groups = pl.groups;
+    da.slot_floats = static_cast<int>(pl.slot_floats);
+    da.group_floats = static_cast<int64_t>(pl.slots * pl.slot_floats);
     st = hip_status(ga::launch_decode(da, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch,
                                       static_cast<hipStream_t>(stream), g_prof_on ? &record_decode : nullptr),
                     "decode launch");

@@ -391,10 +391,31 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
   using C = DecodeCfg<T, D, G, SHARED, Q8, PRE>;
   static_assert(C::KT == kDecodeTile, "tile size");
   const int kSlot = a.slot_floats;
-  const int ncol = G * a.n_tok;   // query columns: column c is token tok0 + c / G, head c % G (<= 16)
   __shared__ __attribute__((aligned(4096))) char smem[C::kLdsBytes];
 
-  const int wg = blockIdx.x, P = gridDim.x;
+  // Column groups: with two, group g takes query columns 16g .. 16g + 15 (its
+  // tokens), with its own workgroups and partials; workgroup w of each group
+  // streams the same tiles.  Workgroups are dealt to the XCDs in turn, so the
+  // two groups' workgroup w run as w' and w' + 8 of the grid: on one XCD, at
+  // about the same time, and the second reads the tiles from its L2.
+  const int P = static_cast<int>(gridDim.x) / a.n_groups;   // workgroups per group
+  int wg = static_cast<int>(blockIdx.x), grp = 0;
+  if (a.n_groups == 2) {
+    if (P % 8 == 0) {
+      const int x = wg % 8, i = wg / 8;
+      grp = i % 2;
+      wg = x + 8 * (i / 2);
+    } else {
+      grp = wg / P;
+      wg %= P;
+    }
+  }
+  constexpr int kGroupTokens = 16 / G;
+  const int tok0 = a.tok0 + grp * kGroupTokens;   // the group's tokens tok0 .. tok0 + n_tok - 1
+  const int n_tok = min(kGroupTokens, a.n_tok - grp * kGroupTokens);
+  if (n_tok <= 0) return;
+  float* const partials = a.partials + grp * a.group_floats;
+  const int ncol = G * n_tok;   // query columns: column c is token tok0 + c / G, head c % G (<= 16)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & 63;
   constexpr int kThreads = C::kWaves * 64;
@@ -427,7 +448,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
     }
     if (bb < a.batch) {
       const int excl = before + incl - n;
-      if (wg == 0) a.tile_prefix[bb] = excl;
+      if (wg == 0 && grp == 0) a.tile_prefix[bb] = excl;
       const int lo = a.n_kv_heads * excl;
       if (n > 0 && t_begin >= lo && t_begin < lo + a.n_kv_heads * n) {
         misc[8] = bb;
@@ -438,7 +459,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
     run += block;
     __syncthreads();
   }
-  if (wg == 0 && threadIdx.x == 0) a.tile_prefix[a.batch] = run;
+  if (wg == 0 && grp == 0 && threadIdx.x == 0) a.tile_prefix[a.batch] = run;
   if (t_begin >= t_end) return;
   Seg cur;
   cur.b = misc[8];
@@ -544,7 +565,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
     {
       const int L = a.seq_lens[cur.b];
       for (int h = wave; h < 16; h += C::kWaves) {
-        const int tok = a.tok0 + h / G;
+        const int tok = tok0 + h / G;
         const T* __restrict__ q = static_cast<const T*>(a.q) +
             ((static_cast<int64_t>(cur.b) * a.q_len + (h < ncol ? tok : 0)) * a.n_q_heads + cur.kvh * G + h % G) * D;
         float x[kPairsPerLane][2];
@@ -607,9 +628,9 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
     // key_lim = P + 1.  Windowed layers: slot s of the ring holds position
     // base + s, or base + s - cache_cap past the newest slot h = (L - 1) mod
     // cache_cap, and is seen when P - W < position <= P.
-    const int key_lim = cur.keys - ((hcol < ncol) ? a.q_len - 1 - (a.tok0 + hcol / G) : 0);
+    const int key_lim = cur.keys - ((hcol < ncol) ? a.q_len - 1 - (tok0 + hcol / G) : 0);
     const int L_cur = a.seq_lens[cur.b];
-    const int col_pos = L_cur - a.q_len + ((hcol < ncol) ? a.tok0 + hcol / G : a.q_len - 1);
+    const int col_pos = L_cur - a.q_len + ((hcol < ncol) ? tok0 + hcol / G : a.q_len - 1);
     const int ring_h = a.window > 0 ? (L_cur - 1) % a.cache_cap : 0;
     const int ring_base = L_cur - 1 - ring_h;
 
@@ -740,7 +761,7 @@ __global__ __launch_bounds__((DecodeCfg<T, D, G, SHARED, Q8, PRE>::kWaves * 64),
     // segment) pair that exists, as a workgroup's segments begin where the
     // previous workgroup's end.  A wave without tiles here leaves m = -inf.
     const float l = sum_across_kg(l_part);
-    float* slot = a.partials + static_cast<size_t>(C::kWaves * (wg + seg) + wave) * kSlot;
+    float* slot = partials + static_cast<size_t>(C::kWaves * (wg + seg) + wave) * kSlot;
     if (hcol < ncol) {
 #pragma unroll
       for (int t = 0; t < C::kDBlocks; ++t) *reinterpret_cast<f32x4*>(slot + hcol * D + 16 * t + 4 * kg) = o[t];
@@ -760,14 +781,19 @@ template <typename T, int D, int G, bool SHARED>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   using C = DecodeCfg<T, D, G, SHARED>;
   const int kSlot = a.slot_floats;
-  const int ncol = G * a.n_tok;
+  const int ncol_all = G * a.n_tok;   // the launch's columns, 16 per column group
   __shared__ float wgt[1024];
   __shared__ float red[256];
-  const int seg = blockIdx.x / ncol, h = blockIdx.x % ncol;   // h: column (token tok0 + h / G, head h % G)
+  const int seg = blockIdx.x / ncol_all, hc = blockIdx.x % ncol_all;
+  constexpr int kGroupTokens = 16 / G;
+  const int grp = hc / 16, h = hc % 16;   // h: column of group grp (token h / G of the group, head h % G)
+  const int ncol = G * min(kGroupTokens, a.n_tok - grp * kGroupTokens);
+  const float* __restrict__ partials = a.partials + grp * a.group_floats;
   const int b = seg / a.n_kv_heads, kvh = seg % a.n_kv_heads;
   const int t = threadIdx.x;
   T* __restrict__ out = static_cast<T*>(a.out) +
-      ((static_cast<int64_t>(b) * a.q_len + a.tok0 + h / G) * a.n_q_heads + kvh * G + h % G) * D;
+      ((static_cast<int64_t>(b) * a.q_len + a.tok0 + grp * kGroupTokens + h / G) * a.n_q_heads + kvh * G + h % G) *
+          D;
   const int keys = decode_keys(a, b);
   if (keys < 0) {
     for (int d = t; d < D; d += 256) out[d] = from_f32<T>(NAN);
@@ -781,7 +807,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int w_hi = static_cast<int>((static_cast<int64_t>(t_seg + n) * P - 1) / t_all);
   const int count = (w_hi - w_lo + 1) * C::kWaves;    // <= kWaves * P <= 1024
   auto slot = [&](int i) {
-    return a.partials + static_cast<size_t>(C::kWaves * (w_lo + i / C::kWaves + seg) + i % C::kWaves) * kSlot;
+    return partials + static_cast<size_t>(C::kWaves * (w_lo + i / C::kWaves + seg) + i % C::kWaves) * kSlot;
   };
   // A workgroup with an empty share (fewer tiles than workgroups) wrote nothing.
   auto written = [&](int i) {
@@ -844,7 +870,8 @@ template <typename T, int D, int G, bool SHARED, bool Q8 = false, bool PRE = fal
 static hipError_t launch_one(const DecodeArgs& a, hipStream_t s, LaunchTimer timer) {
   using C = DecodeCfg<T, D, G, SHARED, Q8, PRE>;
   if (timer) timer(s, 2, true);
-  hipLaunchKernelGGL((decode_kernel<T, D, G, SHARED, Q8, PRE>), dim3(a.n_wgs), dim3(C::kWaves * 64), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<T, D, G, SHARED, Q8, PRE>), dim3(a.n_wgs * a.n_groups), dim3(C::kWaves * 64), 0,
+                     s, a);
   hipError_t e = hipGetLastError();
   if (timer) timer(s, 2, false);
   if (e != hipSuccess) return e;
@@ -908,7 +935,7 @@ static int waves_of() {
 }
 
 bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, int n_kv_heads,
-                 int max_tiles_per_seq, int n_cus, int q_len, DecodePlan* plan) {
+                 int max_tiles_per_seq, int n_cus, int q_len, int groups, DecodePlan* plan) {
   int waves = 0;
   if (dtype == 0 && head_dim == 512) waves = kv_shared ? waves_of<bf16, 512, true>() : waves_of<bf16, 512, false>();
   if (dtype == 0 && head_dim == 256) waves = kv_shared ? waves_of<bf16, 256, true>() : waves_of<bf16, 256, false>();
@@ -920,14 +947,18 @@ bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, i
   // total.
   const int64_t tiles_ub = static_cast<int64_t>(batch) * n_kv_heads * max_tiles_per_seq;
   const int64_t by_work = (tiles_ub + 2 * waves - 1) / (2 * waves);
+  // With two column groups each group gets half the CUs (a multiple of 8, so
+  // that the groups' workgroups pair up on the XCDs).
   int64_t wgs = n_cus < 1 ? 1 : n_cus;
+  if (groups == 2) wgs = wgs >= 16 ? wgs / 16 * 8 : (wgs + 1) / 2;
   wgs = wgs > 1024 / waves ? 1024 / waves : wgs;
   wgs = wgs > by_work ? by_work : wgs;
   plan->waves = waves;
+  plan->groups = groups;
   plan->n_wgs = static_cast<int>(wgs < 1 ? 1 : wgs);
   plan->prefix_bytes = (static_cast<size_t>(batch + 1) * 4 + 255) / 256 * 256;
   plan->slots = static_cast<size_t>(waves) * (plan->n_wgs + static_cast<size_t>(batch) * n_kv_heads);
-  plan->slot_floats = static_cast<size_t>(q_len) * group * head_dim + 64;
+  plan->slot_floats = static_cast<size_t>(q_len < 16 / group ? q_len : 16 / group) * group * head_dim + 64;
   return true;
 }
 

@@ -81,27 +81,31 @@ struct DecodeArgs {
   float* partials;         // [slots][slot_floats] fp32: o per column, then (m, l) per column
   int batch, n_q_heads, n_kv_heads, n_rot, window, cache_cap, max_seq_len;
   int q_len;               // query tokens per sequence: the last q_len positions (1 = one token)
-  int tok0, n_tok;         // this launch's tokens tok0 .. tok0 + n_tok - 1 (G n_tok <= 16 query columns)
+  int tok0, n_tok;         // this launch's tokens tok0 .. tok0 + n_tok - 1 (G n_tok <= 16 n_groups columns)
+  int n_groups;            // column groups of 16 query columns, each with its own workgroups and partials
+  int64_t group_floats;    // partials of one column group (slots x slot_floats)
   const float* k_scales;   // int8 K=V cache: per-row scales [B][Hkv][cache_cap] (else null)
   const void* k_heads;     // pre-rotated K=V cache: heads [B][Hkv][cache_cap][2 n_rot] (else null)
   int slot_floats;         // q_len * G * D + 64
-  int n_wgs;               // split-K workgroups (the grid)
+  int n_wgs;               // split-K workgroups per column group (the grid is n_groups n_wgs)
   float eps;
   float qk_scale_log2;
   double log2_theta;
 };
 
-// Launch shape and scratch of one decode call: n_wgs workgroups of `waves`
-// waves split the tiles evenly; `slots` partial results of slot_floats each.
+// Launch shape and scratch of one decode call: per column group, n_wgs
+// workgroups of `waves` waves split the tiles evenly and `slots` partial
+// results of slot_floats each.
 struct DecodePlan {
-  int waves, n_wgs;
+  int waves, n_wgs, groups;
   size_t prefix_bytes;     // tile_prefix, padded to 256 bytes
   size_t slots, slot_floats;
-  size_t bytes() const { return prefix_bytes + slots * slot_floats * 4; }
+  size_t bytes() const { return prefix_bytes + groups * slots * slot_floats * 4; }
 };
 // Returns false if the configuration has no decode kernel.
+// groups: column groups per launch (1, or 2 for 17..32 query columns).
 bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, int n_kv_heads,
-                 int max_tiles_per_seq, int n_cus, int q_len, DecodePlan* plan);
+                 int max_tiles_per_seq, int n_cus, int q_len, int groups, DecodePlan* plan);
 
 hipError_t launch_rope_table(void* table, int pos_begin, int n_pos, int n_rot, int head_dim, double log2_theta,
                              hipStream_t s);

@@ -278,9 +278,10 @@ ga_status gemma_attn_decode(const ga_layer* layer, int32_t batch,
  * windowed layer needs a ring of cache_cap >= W + q_len - 1 slots (GA_EINVAL
  * otherwise): with W slots the later new tokens would have pushed out keys
  * the earlier ones still see.
- * One pass over the cache serves 16 query columns (q_len tokens x Hq / Hkv
- * heads): more tokens take ceil(q_len (Hq / Hkv) / 16) passes, one after
- * another on the stream, sharing the workspace.
+ * One pass over the cache serves up to 32 query columns (q_len tokens x
+ * Hq / Hkv heads; two groups of 16 that share the tiles): more tokens take
+ * ceil(q_len (Hq / Hkv) / 32) passes, one after another on the stream,
+ * sharing the workspace.
  * q_len = 1 is gemma_attn_decode.  GA_EINVAL for q_len < 1; GA_EUNSUPPORTED
  * when q_len * (Hq / Hkv) > 64.
  */

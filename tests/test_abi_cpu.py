@@ -131,8 +131,10 @@ def test_multi_token_decode_validation(lib):
     assert "1025 slots" in lib.gemma_attn_last_error().decode()
     wsz = lambda layer, B, T, n: lib.gemma_attn_decode_multi_workspace_size(ctypes.byref(layer), B, T, n)
     assert wsz(g, 2, 0, 4096) == 0 and wsz(g, 2, 9, 4096) == 0
-    # past 16 columns the call runs one pass per 16 columns, each with a 16-column plan
-    assert wsz(g, 2, 3, 4096) == wsz(g, 2, 4, 4096) == decode_ws(2, 4, 16, 512, 4096)
+    # 17..32 columns: two column groups of 16, each with its own partials (and half the
+    # workgroups, which the size query does not depend on); more take several launches
+    two_groups = 2 * decode_ws(2, 4, 16, 512, 4096) - 256
+    assert wsz(g, 2, 3, 4096) == wsz(g, 2, 4, 4096) == wsz(g, 2, 8, 4096) == two_groups
     assert wsz(loc, 2, 2, 4096) == decode_ws(2, 16, 4, 256, 4096)     # 2 tokens x G = 2 columns per slot
     # one token is the single-token call; two tokens widen every slot to 2 G d outputs
     assert wsz(g, 2, 1, 4096) == lib.gemma_attn_decode_workspace_size(ctypes.byref(g), 2, 4096)
