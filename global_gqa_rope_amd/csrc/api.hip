@@ -184,19 +184,21 @@ float* q8_scales(const ga_layer* L, const Derived& dv, void* cache, int batch, i
 }
 
 struct PrefillLayout {
-  size_t table, ws_k, ws_v, total;
+  size_t table, table16, ws_k, ws_v, total;
   int seq_pad, kw;
 };
 
-// Workspace: RoPE table [seq_pad][n_rot] (cos, sin) fp32, key rows
-// [B][Hkv][seq_pad][kw], value rows [B][Hkv][seq_pad][d]; each 256-byte aligned.
+// Workspace: RoPE table [seq_pad][n_rot] (cos, sin) fp32, the same table in
+// fp16 (read by the local-layer query prologue), key rows [B][Hkv][seq_pad][kw],
+// value rows [B][Hkv][seq_pad][d]; each 256-byte aligned.
 PrefillLayout prefill_layout(const ga_layer* L, const Derived& dv, int batch, int seq_len) {
   PrefillLayout p;
   p.seq_pad = (seq_len + ga::kPrepTile - 1) / ga::kPrepTile * ga::kPrepTile;
   p.kw = L->kv_shared ? 2 * dv.n_rot : L->head_dim;
   const size_t rows = static_cast<size_t>(batch) * L->n_kv_heads * p.seq_pad;
   p.table = 0;
-  p.ws_k = align_up(static_cast<size_t>(p.seq_pad) * dv.n_rot * 8);
+  p.table16 = align_up(static_cast<size_t>(p.seq_pad) * dv.n_rot * 8);
+  p.ws_k = p.table16 + align_up(static_cast<size_t>(p.seq_pad) * dv.n_rot * 4);
   p.ws_v = p.ws_k + align_up(rows * p.kw * dv.elem);
   p.total = p.ws_v + align_up(rows * L->head_dim * dv.elem);
   return p;
@@ -527,7 +529,7 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
   const bool ring_after = layer->window > 0 && start > 0;
   {
     ProfScope ps(s, 1);
-    st = hip_status(ga::launch_rope_table(ws + lay.table, tile0 * ga::kPrepTile, lay.seq_pad, dv.n_rot,
+    st = hip_status(ga::launch_rope_table(ws + lay.table, ws + lay.table16, tile0 * ga::kPrepTile, lay.seq_pad, dv.n_rot,
                                           layer->head_dim, dv.log2_theta, s),
                     "rope table launch");
     ga::PrepArgs pa{};
@@ -555,7 +557,8 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
   if (st != GA_OK) return st;
 
   ga::PrefillArgs fa{};
-  fa.q = q; fa.q_gain = q_gain; fa.rope_table = ws + lay.table; fa.ws_k = ws + lay.ws_k; fa.ws_v = ws + lay.ws_v;
+  fa.q = q; fa.q_gain = q_gain; fa.rope_table = ws + lay.table; fa.rope_table16 = ws + lay.table16;
+  fa.table_rows = lay.seq_pad; fa.ws_k = ws + lay.ws_k; fa.ws_v = ws + lay.ws_v;
   fa.out = out; fa.seq_len = seq_len; fa.seq_pad = lay.seq_pad; fa.n_q_heads = layer->n_q_heads;
   fa.n_kv_heads = layer->n_kv_heads; fa.n_rot = dv.n_rot; fa.window = layer->window; fa.eps = layer->norm_eps;
   fa.q_pos0 = start;

@@ -60,6 +60,8 @@ struct PrefillArgs {
   const void* q;
   const void* q_gain;
   const void* rope_table;
+  const void* rope_table16;   // the same (cos, sin) pairs in fp16, [rows][n_rot]
+  int table_rows;
   const void* ws_k;        // see PrepArgs
   const void* ws_v;        // K=V layers' value rows (separate-V layers read v)
   const void* v;           // separate-V layers: v [B][S][Hkv][d] read in place (null: ws_v holds it)
@@ -107,7 +109,7 @@ struct DecodePlan {
 bool plan_decode(int dtype, int head_dim, int group, int kv_shared, int batch, int n_kv_heads,
                  int max_tiles_per_seq, int n_cus, int q_len, int groups, DecodePlan* plan);
 
-hipError_t launch_rope_table(void* table, int pos_begin, int n_pos, int n_rot, int head_dim, double log2_theta,
+hipError_t launch_rope_table(void* table, void* table16, int pos_begin, int n_pos, int n_rot, int head_dim, double log2_theta,
                              hipStream_t s);
 hipError_t launch_prefill_prep(const PrepArgs& a, int dtype, int head_dim, int batch, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, int dtype, int head_dim, int batch, hipStream_t s);

@@ -77,7 +77,17 @@ struct PrefillCfg {
                                  : (3 * kStageBytes <= kLdsCap && kMaxStages >= 3) ? 3
                                  : (2 * kStageBytes <= kLdsCap)                    ? 2
                                                                                    : 1;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
+  // Local layers stage the (cos, sin) rows of their query positions in fp16 in
+  // the LDS the prologue does not use yet (the last stage and past it): each
+  // wave copies its PW positions' rows with whole-row loads, and each lane
+  // then reads its pairs from LDS instead of 32 scattered rows from memory.
+  static constexpr bool kTabLds = sizeof(T) == 2 && kRB == 2 && !SHARED && kStages == 4 &&
+                                  (kStages - 1) * kStageBytes + kWaves * PW * (D / 2 * 4) <= kLdsCap;
+  static constexpr int kTabRow = D / 2 * 4;                     // one position's pairs (full rotation)
+  static constexpr int kTabOff = (kStages - 1) * kStageBytes;
+  static constexpr int kTabBytes = kTabLds ? kWaves * PW * kTabRow : 0;
+  static constexpr int kLdsBytes = kTabLds && kTabOff + kTabBytes > kStages * kStageBytes ? kTabOff + kTabBytes
+                                                                                          : kStages * kStageBytes;
   static constexpr int kDmaK = kKBytes / 1024, kDmaV = kVBytes / 1024;
   static constexpr int kDmaPerWave = (kDmaK + kDmaV) / kWaves;
   // Key fragment reads in flight (fewer with two row blocks, whose second
@@ -85,6 +95,7 @@ struct PrefillCfg {
   static constexpr int kKAhead = kRB == 2 ? 4 : 6;
   static constexpr int kVAhead = 4;
   static_assert(kLdsBytes <= kLdsCap, "LDS budget");
+  static_assert(!kTabLds || (kTabRow % 512 == 0 && PW % 2 == 0), "table rows: two per copy instruction");
   static_assert((kDmaK + kDmaV) % kWaves == 0 && kKBytes % 1024 == 0, "tile copy split");
   static_assert(kKBytes % kVRowBytes == 0 && kStageBytes % kVRowBytes == 0, "row alignment for the swizzle");
   static_assert(kKRowBytes >= 256 && kVRowBytes >= 256, "row swizzle needs 16 chunks per row");
@@ -705,6 +716,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   // query when it is used (a slow path that exists for exact tests).
   constexpr bool kQRegs = sizeof(T) == 2;
   constexpr int kRB = C::kRB;
+  lds_char* const tab = (lds_char*)smem + C::kTabOff + wave * C::PW * C::kTabRow;   // this wave's table rows
   static_assert(kQRegs || kRB == 1, "the fp32 build keeps one row block");
   Frag8<T> qf[kRB][kQRegs ? C::kQSteps : 1];
   const T* __restrict__ qrow[kRB];
@@ -729,6 +741,24 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int u = 0; u < C::kQSteps; ++u) load_frag(qf[rb][u], qrow[rb] + 16 * u + 8 * h);
+      if constexpr (C::kTabLds) {
+        // rows p0 + wave PW .. + PW - 1, two per instruction; chunk c (pairs
+        // 4c .. 4c + 3) of row r lands in slot c ^ (r & 15) so the lanes'
+        // reads below spread over the banks.  With n_rot < d / 2 the chunks
+        // past n_rot hold the next row's pairs and are not used; rows past
+        // the table read zeros.  At most 4M positions of 128 pairs: the byte
+        // offsets stay below 2^32.
+        const uint32_t row_bytes = static_cast<uint32_t>(a.n_rot) * 4;
+        const BufRsrc rt = make_rsrc(a.rope_table16, static_cast<uint32_t>(a.table_rows) * row_bytes);
+        constexpr int kSlots = C::kTabRow / 16;
+#pragma unroll
+        for (int i = 0; i < C::PW / 2; ++i) {
+          const int r = 2 * i + lane / kSlots, slot = lane % kSlots;
+          const uint32_t pos_r = static_cast<uint32_t>(p0 + wave * C::PW + r);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, tab + i * 1024, 16,
+                                                   pos_r * row_bytes + ((slot ^ (r & 15)) << 4), 0, 0, 0);
+        }
+      }
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < C::kStages - 1; ++i)
@@ -758,6 +788,11 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   QSource<T, D> qs[kRB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) qs[rb] = QSource<T, D>{qf[rb], qrow[rb], gq, qtable[rb], rs[rb], a.n_rot};
+  if constexpr (C::kTabLds) {
+    // the table rows have landed once at most the first tiles' copies (issued
+    // after them) are in flight; each wave reads only the rows it copied
+    wait_vm_le<(C::kStages - 1) * C::kDmaPerWave>();
+  }
   if constexpr (kQRegs) {
     // Gain and rotation of the register fragments.  The gains and (cos, sin)
     // pairs of kBatch steps are all loaded before any is used, so their round
@@ -777,9 +812,21 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-          if (u0 + i < kRotSteps)
+          if (u0 + i < kRotSteps) {
+            if constexpr (C::kTabLds) {
+              // row r of the wave's block: pairs 8u + 4h .. +3 are chunk 2u + h
+              const int r = C::kRows * rb / G + m / G;
+              typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+              const h8 v = *(const __attribute__((address_space(3))) h8*)(
+                  tab + r * C::kTabRow + (((2 * (u0 + i) + h) ^ (r & 15)) << 4));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cs[rb][i][j] = qtable[rb][8 * (u0 + i) + 4 * h + j];
+              for (int j = 0; j < 4; ++j)
+                cs[rb][i][j] = f32x2{static_cast<float>(v[2 * j]), static_cast<float>(v[2 * j + 1])};
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) cs[rb][i][j] = qtable[rb][8 * (u0 + i) + 4 * h + j];
+            }
+          }
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll

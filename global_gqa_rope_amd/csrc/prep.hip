@@ -7,15 +7,21 @@ namespace ga {
 
 // table[pos][pair] = (cos, sin)(pos * theta^(-2 pair / d)), fp64 math.
 // Rows pos_begin .. n_pos - 1 (earlier rows are not read).
-__global__ void rope_table_kernel(f32x2* __restrict__ table, int pos_begin, int n_pos, int n_rot,
-                                  int head_dim, double log2_theta) {
+__global__ void rope_table_kernel(f32x2* __restrict__ table, uint32_t* __restrict__ table16, int pos_begin,
+                                  int n_pos, int n_rot, int head_dim, double log2_theta) {
   const int64_t first = static_cast<int64_t>(pos_begin) * n_rot;
   const int64_t total = static_cast<int64_t>(n_pos) * n_rot;
   for (int64_t i = first + blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int pos = static_cast<int>(i / n_rot);
     const int pair = static_cast<int>(i % n_rot);
-    table[i] = rope_cos_sin(static_cast<double>(pos) * rope_omega(pair, head_dim, log2_theta));
+    const f32x2 cs = rope_cos_sin(static_cast<double>(pos) * rope_omega(pair, head_dim, log2_theta));
+    table[i] = cs;
+    if (table16) {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 v = {static_cast<_Float16>(cs[0]), static_cast<_Float16>(cs[1])};
+      table16[i] = __builtin_bit_cast(uint32_t, v);
+    }
   }
 }
 
@@ -318,13 +324,13 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
 
 // ---- launchers ---------------------------------------------------------------
 
-hipError_t launch_rope_table(void* table, int pos_begin, int n_pos, int n_rot, int head_dim, double log2_theta,
+hipError_t launch_rope_table(void* table, void* table16, int pos_begin, int n_pos, int n_rot, int head_dim, double log2_theta,
                              hipStream_t s) {
   if (n_rot == 0 || n_pos <= pos_begin) return hipSuccess;
   const int64_t total = static_cast<int64_t>(n_pos - pos_begin) * n_rot;
   const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 4096));
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, s, static_cast<f32x2*>(table),
-                     pos_begin, n_pos, n_rot, head_dim, log2_theta);
+                     static_cast<uint32_t*>(table16), pos_begin, n_pos, n_rot, head_dim, log2_theta);
   return hipGetLastError();
 }
 
