@@ -184,13 +184,14 @@ float* q8_scales(const ga_layer* L, const Derived& dv, void* cache, int batch, i
 }
 
 struct PrefillLayout {
-  size_t table, table16, ws_k, ws_v, total;
+  size_t table, table16, ws_k, ws_v, ws_kn, total;
   int seq_pad, kw;
 };
 
 // Workspace: RoPE table [seq_pad][n_rot] (cos, sin) fp32, the same table in
 // fp16 (read by the local-layer query prologue), key rows [B][Hkv][seq_pad][kw],
-// value rows [B][Hkv][seq_pad][d]; each 256-byte aligned.
+// value rows [B][Hkv][seq_pad][d], the largest squared key length of each tile
+// of key rows [B][Hkv][seq_pad / kPrepTile] fp32; each 256-byte aligned.
 PrefillLayout prefill_layout(const ga_layer* L, const Derived& dv, int batch, int seq_len) {
   PrefillLayout p;
   p.seq_pad = (seq_len + ga::kPrepTile - 1) / ga::kPrepTile * ga::kPrepTile;
@@ -200,7 +201,8 @@ PrefillLayout prefill_layout(const ga_layer* L, const Derived& dv, int batch, in
   p.table16 = align_up(static_cast<size_t>(p.seq_pad) * dv.n_rot * 8);
   p.ws_k = p.table16 + align_up(static_cast<size_t>(p.seq_pad) * dv.n_rot * 4);
   p.ws_v = p.ws_k + align_up(rows * p.kw * dv.elem);
-  p.total = p.ws_v + align_up(rows * L->head_dim * dv.elem);
+  p.ws_kn = p.ws_v + align_up(rows * L->head_dim * dv.elem);
+  p.total = p.ws_kn + align_up(rows / ga::kPrepTile * sizeof(float));
   return p;
 }
 
@@ -544,6 +546,7 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
     pa.write_cache = !ring_after;
     pa.k_scales = q8_scales(layer, dv, k_cache, batch, cache_cap);
     pa.k_heads = pre_heads(layer, dv, k_cache, batch, cache_cap);
+    pa.ws_kn = reinterpret_cast<float*>(ws + lay.ws_kn);
     if (st == GA_OK)
       st = hip_status(ga::launch_prefill_prep(pa, layer->dtype, layer->head_dim, batch, s), "prefill prep launch");
     if (st == GA_OK && ring_after && k_cache) {
@@ -563,6 +566,7 @@ static ga_status prefill_impl(const ga_layer* layer, int32_t batch, int32_t star
   fa.n_kv_heads = layer->n_kv_heads; fa.n_rot = dv.n_rot; fa.window = layer->window; fa.eps = layer->norm_eps;
   fa.q_pos0 = start;
   fa.v = v_in_place ? v : nullptr;
+  fa.ws_kn = reinterpret_cast<const float*>(ws + lay.ws_kn);
   fa.qk_scale_log2 = dv.scale * 1.4426950408889634f;
   ProfScope ps(s, 0);
   return hip_status(ga::launch_prefill_attn(fa, layer->dtype, layer->head_dim, dv.group, layer->kv_shared, batch, s),

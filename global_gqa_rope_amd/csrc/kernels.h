@@ -39,6 +39,7 @@ struct PrepArgs {
   int write_cache;         // write the new rows into the caches
   float* k_scales;         // int8 K=V cache: per-row scales [B][Hkv][cache_cap] (else null)
   void* k_heads;           // pre-rotated K=V cache: heads [B][Hkv][cache_cap][2 n_rot] (else null)
+  float* ws_kn;            // [B][Hkv][seq_pad / kPrepTile] largest squared norm of a tile's key rows (with write_ws)
   float eps;
 };
 
@@ -65,6 +66,7 @@ struct PrefillArgs {
   const void* ws_k;        // see PrepArgs
   const void* ws_v;        // K=V layers' value rows (separate-V layers read v)
   const void* v;           // separate-V layers: v [B][S][Hkv][d] read in place (null: ws_v holds it)
+  const float* ws_kn;      // see PrepArgs
   void* out;
   int seq_len, seq_pad, n_q_heads, n_kv_heads, n_rot, window;
   int q_pos0;              // position of q's (and out's) first row; keys from position 0

@@ -92,7 +92,7 @@ struct PrefillCfg {
   static constexpr int kDmaPerWave = (kDmaK + kDmaV) / kWaves;
   // Key fragment reads in flight (fewer with two row blocks, whose second
   // query block takes the registers) and value fragments (two reads each).
-  static constexpr int kKAhead = kRB == 2 ? 4 : 6;
+  static constexpr int kKAhead = kRB == 2 ? 2 : 6;
   static constexpr int kVAhead = 4;
   static_assert(kLdsBytes <= kLdsCap, "LDS budget");
   static_assert(!kTabLds || (kTabRow % 512 == 0 && PW % 2 == 0), "table rows: two per copy instruction");
@@ -410,7 +410,9 @@ __device__ __forceinline__ void qk_prefetch(Frag8<T> (&kf)[C::kKAhead], const ld
 // fragments read kKAhead steps ahead of the MFMAs.  `copy(k)`, k < NC, goes
 // after every (kQSteps / NC)-th MFMA, and `work(u)` (other, independent work)
 // after MFMA u in program order.
-template <typename C, typename T, int D, int NC, typename CopyFn, typename WorkFn>
+// PRE: the kKAhead prefetch reads are in the same scheduling region (no
+// branch between them and this run), so the pattern places them first.
+template <typename C, typename T, int D, int NC, bool PRE = false, typename CopyFn, typename WorkFn>
 __device__ __forceinline__ void qk_run(f32x16 (&s)[C::kRB], Frag8<T> (&kf)[C::kKAhead], const lds_char* cur,
                                        const LaneOffsets& lo, const QSource<T, D> (&qs)[C::kRB], int h,
                                        CopyFn&& copy, WorkFn&& work) {
@@ -429,7 +431,7 @@ __device__ __forceinline__ void qk_run(f32x16 (&s)[C::kRB], Frag8<T> (&kf)[C::kK
     work(u);
   }
   if constexpr (sizeof(T) == 2)
-    interleave_reads_mfma<C::kKAhead, C::kQSteps, 1, NC, kStride, false, C::kRB>();
+    interleave_reads_mfma<C::kKAhead, C::kQSteps, 1, NC, kStride, PRE, C::kRB>();
 }
 
 // Scores of an edge tile masked: register r of this lane is key
@@ -474,16 +476,32 @@ __device__ __forceinline__ float update_max(const float (&sv)[16], RowState<NB>&
   return rs.m_run == -INFINITY ? 0.f : rs.m_run;
 }
 
-// P = exp2(S - m) into the two B operands of the PV MFMAs (score registers
-// 8c .. 8c+7 form operand c), and the lane's part of the row sum.
+// Softmax weight r (of the lane's 16) into the B operands of the PV MFMAs
+// (score registers 8c .. 8c+7 form operand c), and into the lane's part of
+// the row sum.  bf16: the row sum adds the rounded weights the MFMAs use, a
+// pair at a time (paired dot product with ones), so the weights of a row sum
+// to one after the division; a row with one visible key returns its value
+// row exactly.
+__device__ __forceinline__ void put_weight(Frag8<bf16> (&pf)[2], int r, float p, float& l) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  frag_set(pf[r / 8], r % 8, p);
+  if (r % 2 == 1) {
+    const bf16x2 w = {pf[r / 8].v[r % 8 - 1], pf[r / 8].v[r % 8]};
+    const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    l = __builtin_amdgcn_fdot2_f32_bf16(w, one, l, false);
+  }
+}
+__device__ __forceinline__ void put_weight(Frag8<float> (&pf)[2], int r, float p, float& l) {
+  frag_set(pf[r / 8], r % 8, p);
+  l += p;
+}
+
+// P = exp2(S - m) into the two B operands of the PV MFMAs, and the lane's
+// part of the row sum.
 template <typename T>
 __device__ __forceinline__ void tile_exps(Frag8<T> (&pf)[2], const float (&sv)[16], float m_use, float& l) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = __builtin_amdgcn_exp2f(sv[r] - m_use);
-    l += p;
-    frag_set(pf[r / 8], r % 8, p);
-  }
+  for (int r = 0; r < 16; ++r) put_weight(pf, r, __builtin_amdgcn_exp2f(sv[r] - m_use), l);
 }
 
 // O^T += V^T P^T from the value rows of the stage at `st`: step f = 2t + c
@@ -574,15 +592,20 @@ __device__ __forceinline__ void tile_step(const lds_char* __restrict__ cur, lds_
 // PV, so that the exponentials of tile i run under the QK^T MFMAs of tile
 // i + 1 instead of stalling the matrix unit.  The copy of tile next_tile into
 // `nxt` spreads over those MFMAs.  NEXT = false: the last tile, no QK^T and no
-// copy.  All three stages are distinct (restrict, as for tile_step).
-template <typename C, typename T, int D, bool MASK, bool NEXT>
+// copy.  All three stages are distinct (restrict, as for tile_step).  s_in
+// and s_out may be one array (the scores are copied first); distinct arrays
+// in alternate steps save that copy.
+// FIXED: the wave's scores are known to lie within +-kScoreBound (see
+// score_bound_ok), so P = 2^S needs no running max: no row max, no rescale
+// test and no subtraction.
+template <typename C, typename T, int D, bool MASK, bool NEXT, bool FIXED>
 __device__ __forceinline__ void pipe_step(const lds_char* __restrict__ kcur, const lds_char* __restrict__ vcur,
                                           lds_char* __restrict__ nxt, const char* kbase, const char* vbase,
                                           uint32_t kspan, uint32_t vspan, uint32_t vstride, int next_tile, int wave,
                                           int lane,
                                           const LaneOffsets& lo, const QSource<T, D> (&qs)[C::kRB], int key0,
                                           const int (&pos)[C::kRB], int window, RowState<C::kDBlocks> (&rs)[C::kRB],
-                                          f32x16 (&s)[C::kRB]) {
+                                          const f32x16 (&s_in)[C::kRB], f32x16 (&s_out)[C::kRB]) {
   const int h = lane >> 5;
   Frag8<T> kf[C::kKAhead];
   if constexpr (NEXT) qk_prefetch<C, T, D>(kf, kcur, lo);
@@ -591,22 +614,21 @@ __device__ __forceinline__ void pipe_step(const lds_char* __restrict__ kcur, con
 #pragma unroll
   for (int rb = 0; rb < C::kRB; ++rb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[rb][r] = s[rb][r];
+    for (int r = 0; r < 16; ++r) sv[rb][r] = s_in[rb][r];
     if constexpr (MASK) mask_scores(sv[rb], key0, pos[rb], window, h);
-    m_use[rb] = update_max(sv[rb], rs[rb]);
+    if constexpr (FIXED) m_use[rb] = 0.f;
+    else m_use[rb] = update_max(sv[rb], rs[rb]);
   }
   Frag8<T> pf[C::kRB][2];
   if constexpr (NEXT) {
     // exponential r of every row block after QK^T step r
     const TileCopier<C> copy = make_copier<C>(kbase, vbase, kspan, vspan, vstride, nxt, next_tile, wave, lane);
-    qk_run<C, T, D, C::kDmaPerWave>(s, kf, kcur, lo, qs, h, copy, [&](int u) {
+    // without the rescale test's branch the prefetch reads share the region
+    qk_run<C, T, D, C::kDmaPerWave, FIXED>(s_out, kf, kcur, lo, qs, h, copy, [&](int u) {
       if (u < 16) {
 #pragma unroll
-        for (int rb = 0; rb < C::kRB; ++rb) {
-          const float p = __builtin_amdgcn_exp2f(sv[rb][u] - m_use[rb]);
-          rs[rb].l_part += p;
-          frag_set(pf[rb][u / 8], u % 8, p);
-        }
+        for (int rb = 0; rb < C::kRB; ++rb)
+          put_weight(pf[rb], u, __builtin_amdgcn_exp2f(FIXED ? sv[rb][u] : sv[rb][u] - m_use[rb]), rs[rb].l_part);
       }
     });
   } else {
@@ -614,6 +636,23 @@ __device__ __forceinline__ void pipe_step(const lds_char* __restrict__ kcur, con
     for (int rb = 0; rb < C::kRB; ++rb) tile_exps(pf[rb], sv[rb], m_use[rb], rs[rb].l_part);
   }
   pv_tile<C, T>(vcur, lo, pf, rs, lane);
+}
+
+// Scores S = q~ . k~ (q~ already scaled by softmax scale * log2(e)) satisfy
+// |S| <= |q~| max |k~| (Cauchy-Schwarz).  QKNorm makes both lengths about
+// sqrt(d) times the gains' rms, so with moderate gains and the 1/sqrt(d)
+// scale the bound is a few tens: then P = 2^S lies in [2^-kScoreBound,
+// 2^kScoreBound] and needs no running max (a constant shift of the
+// exponent does not change the softmax).  Row sums stay below 2^(kScoreBound
+// + 22) for 4M keys, far inside fp32.  Rows whose bound is larger keep the
+// online max.
+constexpr float kScoreBound = 40.f;
+// True when every row of the wave is within the bound: qn2 its squared query
+// length, kn2 the largest squared key length of the tiles it reads.  2% of
+// margin covers the rounding of the sums of squares; NaN gives false.
+__device__ __forceinline__ bool score_bound_ok(float qn2, float kn2) {
+  const float b2 = qn2 * kn2 * 1.0404f;
+  return !__any(!(b2 <= kScoreBound * kScoreBound));
 }
 
 template <typename T, int D, int G, bool SHARED>
@@ -729,6 +768,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     qtable[rb] = static_cast<const f32x2*>(a.rope_table) + static_cast<int64_t>(row_valid[rb] ? pos[rb] : 0) * a.n_rot;
   }
   float rs[kRB];
+  // Largest squared key length over the tiles this workgroup reads.
+  const int n_kt = kt_hi - kt_lo;
+  const float* __restrict__ kn_tiles = a.ws_kn + head * (a.seq_pad / C::KT) + kt_lo;
+  float kn2 = 0.f;
   {
     float ss[kRB];
 #pragma unroll
@@ -759,6 +802,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
                                                    pos_r * row_bytes + ((slot ^ (r & 15)) << 4), 0, 0, 0);
         }
       }
+      // the key-length maxima of the first 64 tiles (the rest after the copies)
+      kn2 = lane < n_kt ? kn_tiles[lane] : 0.f;
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int i = 0; i < C::kStages - 1; ++i)
@@ -885,7 +930,32 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   const int hi_begin = max(lo_end, min(kt_hi, (p0 + 1) / C::KT));
   auto stage_of = [&](int t) { return lds + (static_cast<unsigned>(t - kt_lo) % C::kStages) * C::kStageBytes; };
 
+  // Scores within +-kScoreBound for all of the wave's rows: no running max.
+  bool fixed = false;
+  if constexpr (kQRegs && C::kStages >= 3) {
+    for (int i = lane + kWave; i < n_kt; i += kWave) kn2 = fmaxf(kn2, kn_tiles[i]);
+#pragma unroll
+    for (int x = 1; x < kWave; x <<= 1) kn2 = fmaxf(kn2, wave_xor(kn2, x));
+    float qn2 = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      float q2 = 0.f;
+#pragma unroll
+      for (int u = 0; u < C::kQSteps; ++u) q2 = sum_squares(qf[rb][u], q2);
+      qn2 = fmaxf(qn2, sum_halves(q2));
+    }
+    // Rows that see fewer than 64 keys keep the online max: with P = 2^S
+    // every weight is rounded to bf16, where the max-subtracted weight of a
+    // row's largest score is exactly 1, and on rows of a few keys that
+    // difference shows in the outputs (on longer rows the roundings average
+    // out).
+    const bool long_rows = p0 + wave * C::PW >= 63 && (a.window == 0 || a.window >= 64);
+    fixed = long_rows && __builtin_amdgcn_readfirstlane(static_cast<int>(score_bound_ok(qn2, kn2))) != 0;
+  }
+
   if constexpr (C::kStages >= 3) {
+   auto pipeline = [&](auto fx) {
+    constexpr bool FX = decltype(fx)::value;
     // Pipelined: step i runs the softmax and PV of tile i and the QK^T of
     // tile i + 1.  It reads the keys of tile i + 1 and the values of tile i,
     // and copies tile i + kStages - 1 into the stage of tile i - 1, which
@@ -899,7 +969,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       qk_prefetch<C, T, D>(kf, stage_of(kt_lo), lo);
       qk_run<C, T, D, 0>(s, kf, stage_of(kt_lo), lo, qs, h, [](int) {}, [](int) {});
     }
-    auto step = [&](int kt, auto masked) {
+    auto step = [&](int kt, auto masked, const f32x16 (&s_in)[kRB], f32x16 (&s_out)[kRB]) {
       // tile kt + 1 landed (one later tile may be in flight) and is visible
       // to all waves; all waves are past step kt - 1.  A bare barrier: the
       // wait above already covers the copies.
@@ -908,9 +978,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       asm volatile("" ::: "memory");
       // copies of tiles past the workgroup's last one read nothing (an empty range)
       const bool live = kt + C::kStages - 1 < kt_hi;
-      pipe_step<C, T, D, decltype(masked)::value, true>(
+      pipe_step<C, T, D, decltype(masked)::value, true, FX>(
           stage_of(kt + 1), stage_of(kt), stage_of(kt + C::kStages - 1), kbase, vbase, live ? kspan : 0u,
-          live ? vspan : 0u, vstride, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos, a.window, st, s);
+          live ? vspan : 0u, vstride, kt + C::kStages - 1, wave, lane, lo, qs, kt * C::KT, pos, a.window, st, s_in,
+          s_out);
     };
     const int last = kt_hi - 1;
     const int m1 = min(lo_end, last), m2 = max(m1, min(hi_begin, last));
@@ -918,14 +989,21 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
 #pragma nounroll
     for (int phase = 0; phase < 2; ++phase) {
       const int masked_end = phase == 0 ? m1 : last;
-      for (; kt < masked_end; ++kt) step(kt, std::true_type{});
-      if (phase == 0)
-        for (; kt < m2; ++kt) step(kt, std::false_type{});
+      for (; kt < masked_end; ++kt) step(kt, std::true_type{}, s, s);
+      if (phase == 0) {
+        // unmasked tiles two at a time, the scores alternating between two
+        // register sets (no copy of the scores per step)
+        for (; kt < m2; ++kt) step(kt, std::false_type{}, s, s);
+      }
     }
     // The last tile (always an edge): its values landed with its keys, and
     // nothing is copied, so neither a wait nor a barrier.
-    pipe_step<C, T, D, true, false>(stage_of(last + 1), stage_of(last), stage_of(last + C::kStages - 1), kbase,
-                                    vbase, kspan, vspan, vstride, 0, wave, lane, lo, qs, last * C::KT, pos, a.window, st, s);
+    pipe_step<C, T, D, true, false, FX>(stage_of(last + 1), stage_of(last), stage_of(last + C::kStages - 1), kbase,
+                                        vbase, kspan, vspan, vstride, 0, wave, lane, lo, qs, last * C::KT, pos, a.window,
+                                        st, s, s);
+   };
+    if (fixed) pipeline(std::true_type{});
+    else pipeline(std::false_type{});
   } else {
     // One tile per step: wait for it, barrier, then the (masked or plain) step.
     auto run_tile = [&](int kt, auto masked) {

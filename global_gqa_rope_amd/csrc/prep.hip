@@ -208,6 +208,31 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) kout[i][j] = cached_sep ? kin[i][j] : from_f32<T>(x[i][j]);
 
+  // Largest squared length of the tile's key rows, as the attention kernel
+  // reads them (the rounded rotated key; on K=V layers its dims past kw are
+  // the value row's, which the rotation left unchanged).  The attention
+  // kernel bounds its scores with it.
+  if (a.write_ws && a.ws_kn) {
+    __shared__ float wave_max[4];
+    float n2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMine; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) n2 += to_f32(kout[i][j]) * to_f32(kout[i][j]);
+    n2 += wave_xor(n2, 1);
+    n2 += wave_xor(n2, 2);
+    n2 += wave_xor(n2, 4);
+    n2 = fmaxf(n2, wave_xor(n2, 8));
+    n2 = fmaxf(n2, wave_xor(n2, 16));
+    n2 = fmaxf(n2, wave_xor(n2, 32));
+    static_assert(kPrepTile * 8 == 256, "four waves of eight rows");
+    if ((t & (kWave - 1)) == 0) wave_max[t / kWave] = n2;
+    __syncthreads();
+    if (t == 0)
+      a.ws_kn[head_base * (a.seq_pad / kPrepTile) + tile] =
+          fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  }
+
   // Key row: dims 0..kw-1 of the rotated normalised key.
   if (a.write_ws) {
     T* __restrict__ wk = static_cast<T*>(a.ws_k) + row * a.kw;

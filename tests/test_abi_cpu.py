@@ -168,9 +168,10 @@ def test_workspace_sizes_follow_the_layout(lib):
     g = L()
     # tables (S_pad * 64 pairs, 8 B in fp32 and 4 B in fp16) + key rows
     # [B,Hkv,S_pad,128] (the rotated head of a K=V layer) + value rows
-    # [B,Hkv,S_pad,512], bf16
+    # [B,Hkv,S_pad,512], bf16 + the largest squared key length of each
+    # 32-row tile [B,Hkv,S_pad/32], fp32
     s_pad = 32768
-    want = s_pad * 64 * (8 + 4) + 1 * 4 * s_pad * 128 * 2 + 1 * 4 * s_pad * 512 * 2
+    want = s_pad * 64 * (8 + 4) + 1 * 4 * s_pad * 128 * 2 + 1 * 4 * s_pad * 512 * 2 + 1 * 4 * (s_pad // 32) * 4
     assert lib.gemma_attn_prefill_workspace_size(ctypes.byref(g), 1, 32768) == want
     loc = L(hq=32, hkv=16, d=256, window=1024, shared=0, theta=1e4, p=1.0)
     # at most 1024 / waves workgroups: the scratch stops growing with max_seq_len
