@@ -90,10 +90,12 @@ struct PrefillCfg {
                                                                                           : kStages * kStageBytes;
   static constexpr int kDmaK = kKBytes / 1024, kDmaV = kVBytes / 1024;
   static constexpr int kDmaPerWave = (kDmaK + kDmaV) / kWaves;
-  // Key fragment reads in flight (fewer with two row blocks, whose second
-  // query block takes the registers) and value fragments (two reads each).
+  // Key fragment reads in flight and value fragments (two reads each) in
+  // flight: fewer with two row blocks, whose second query block takes the
+  // registers (four and four spilled inside the tile loop; two and two do
+  // not, 1% faster).
   static constexpr int kKAhead = kRB == 2 ? 2 : 6;
-  static constexpr int kVAhead = 4;
+  static constexpr int kVAhead = kRB == 2 ? 2 : 4;
   static_assert(kLdsBytes <= kLdsCap, "LDS budget");
   static_assert(!kTabLds || (kTabRow % 512 == 0 && PW % 2 == 0), "table rows: two per copy instruction");
   static_assert((kDmaK + kDmaV) % kWaves == 0 && kKBytes % 1024 == 0, "tile copy split");
