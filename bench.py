@@ -36,20 +36,20 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 # still match; after any change to them the figure is stale and reads null.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "2315a3c08e0171da",
-                     "bytes": 7862809472},
-    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "2315a3c08e0171da",
-                           "bytes": 10619417690},
-    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "2315a3c08e0171da",
-                           "bytes": 1583837990},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "6fc2be6d049b6f4b",
-                      "bytes": 4288872720},
-    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "6fc2be6d049b6f4b",
-                            "bytes": 4312478888},
-    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "6fc2be6d049b6f4b",
-                                 "bytes": 5355004224},
-    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "6fc2be6d049b6f4b",
-                           "bytes": 2173368972},
+    "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "7316aabfd60968e3",
+                     "bytes": 7979345877},
+    "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "7316aabfd60968e3",
+                           "bytes": 8551456587},
+    "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "7316aabfd60968e3",
+                           "bytes": 1590247957},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2b99507a432f4e75",
+                      "bytes": 4289461833},
+    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2b99507a432f4e75",
+                            "bytes": 4313065684},
+    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2b99507a432f4e75",
+                                 "bytes": 5355695671},
+    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2b99507a432f4e75",
+                           "bytes": 2173548058},
 }
 
 
