@@ -783,7 +783,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int kSlot = a.slot_floats;
   const int ncol_all = G * a.n_tok;   // the launch's columns, 16 per column group
   __shared__ float wgt[1024];
-  __shared__ float red[256];
+  __shared__ float red[8];
   const int seg = blockIdx.x / ncol_all, hc = blockIdx.x % ncol_all;
   constexpr int kGroupTokens = 16 / G;
   const int grp = hc / 16, h = hc % 16;   // h: column of group grp (token h / G of the group, head h % G)
@@ -815,55 +815,74 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     return (t_all * w) / P < (t_all * (w + 1)) / P;
   };
 
+  // Each thread keeps the (m, l) of its slots (at most 4: count <= 1024) in
+  // registers; the max and the sum go across the wave by row-swap moves and
+  // across the 4 waves through LDS, one barrier each.
+  constexpr int kPer = 1024 / 256;
+  float mi[kPer], li[kPer];
   float mx = -INFINITY;
-  for (int i = t; i < count; i += 256)
-    if (written(i)) mx = fmaxf(mx, slot(i)[ncol * D + 2 * h]);
-  red[t] = mx;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] = fmaxf(red[t], red[t + s]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float lsum = 0.f;
-  for (int i = t; i < count; i += 256) {
-    float w = 0.f;
-    if (written(i)) {
-      const float* p = slot(i);
-      const float mi = p[ncol * D + 2 * h];
-      w = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - M);
-      lsum += w * p[ncol * D + 2 * h + 1];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = t + 256 * k;
+    mi[k] = -INFINITY;
+    li[k] = 0.f;
+    if (i < count && written(i)) {
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(slot(i) + ncol * D + 2 * h);
+      mi[k] = ml[0];
+      li[k] = ml[1];
     }
-    wgt[i] = w;
+    mx = fmaxf(mx, mi[k]);
   }
-  red[t] = lsum;
+  const int wave = t >> 6;
+#pragma unroll
+  for (int x = 1; x < kWave; x <<= 1) mx = fmaxf(mx, wave_xor(mx, x));
+  if ((t & (kWave - 1)) == 0) red[wave] = mx;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] += red[t + s];
-    __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float lsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = t + 256 * k;
+    const float w = (mi[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi[k] - M);
+    lsum += w * li[k];
+    if (i < count) wgt[i] = w;
   }
-  const float inv = 1.0f / red[0];
+#pragma unroll
+  for (int x = 1; x < kWave; x <<= 1) lsum += wave_xor(lsum, x);
+  if ((t & (kWave - 1)) == 0) red[4 + wave] = lsum;
+  __syncthreads();
+  const float inv = 1.0f / ((red[4] + red[5]) + (red[6] + red[7]));
   // Every slot below `count` lies in the partials buffer, so its load needs no
   // guard and several can be in flight; a zero weight (a share that wrote
   // nothing, whose slot may hold anything) selects 0 instead of the product.
-  for (int d = t; d < D; d += 256) {
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-    int i = 0;
-    for (; i + 4 <= count; i += 4) {
-      const float v0 = slot(i)[h * D + d], v1 = slot(i + 1)[h * D + d];
-      const float v2 = slot(i + 2)[h * D + d], v3 = slot(i + 3)[h * D + d];
-      o0 += wgt[i] != 0.f ? wgt[i] * v0 : 0.f;
-      o1 += wgt[i + 1] != 0.f ? wgt[i + 1] * v1 : 0.f;
-      o2 += wgt[i + 2] != 0.f ? wgt[i + 2] * v2 : 0.f;
-      o3 += wgt[i + 3] != 0.f ? wgt[i + 3] * v3 : 0.f;
+  // Thread t owns D / 256 consecutive dims (one 8-byte load per slot at
+  // d = 512); eight slots' loads go out together.
+  constexpr int kDims = D / 256;
+  static_assert(kDims == 1 || kDims == 2, "head dim 256 or 512");
+  typedef float fvec __attribute__((ext_vector_type(kDims)));
+  const int d0 = t * kDims;
+  fvec acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = fvec(0.f);
+  int i = 0;
+  for (; i + 8 <= count; i += 8) {
+    fvec v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const fvec*>(slot(i + k) + h * D + d0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float wk = wgt[i + k];
+      acc[k % 4] += wk != 0.f ? wk * v[k] : fvec(0.f);
     }
-    for (; i < count; ++i) {
-      const float v = slot(i)[h * D + d];
-      o0 += wgt[i] != 0.f ? wgt[i] * v : 0.f;
-    }
-    out[d] = from_f32<T>(((o0 + o1) + (o2 + o3)) * inv);
   }
+  for (; i < count; ++i) {
+    const fvec v = *reinterpret_cast<const fvec*>(slot(i) + h * D + d0);
+    const float wk = wgt[i];
+    acc[0] += wk != 0.f ? wk * v : fvec(0.f);
+  }
+  const fvec o = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * inv;
+#pragma unroll
+  for (int k = 0; k < kDims; ++k) out[d0 + k] = from_f32<T>(o[k]);
 }
 
 template <typename T, int D, int G, bool SHARED, bool Q8 = false, bool PRE = false>
