@@ -37,19 +37,19 @@ MI355X_HBM_GBS = 8000.0             # published HBM3E bandwidth
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "global_gqa_rope_amd", "csrc")
 MEASURED_TRAFFIC = {
     "prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "7316aabfd60968e3",
-                     "bytes": 7979345877},
+                     "bytes": 7968733504},
     "local_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "7316aabfd60968e3",
-                           "bytes": 8551456587},
+                           "bytes": 8566853963},
     "chunk_prefill_attn": {"sources": ("prefill.hip", "common.h", "kernels.h"), "digest": "7316aabfd60968e3",
-                           "bytes": 1590247957},
-    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2b99507a432f4e75",
-                      "bytes": 4289461833},
-    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2b99507a432f4e75",
-                            "bytes": 4313065684},
-    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2b99507a432f4e75",
-                                 "bytes": 5355695671},
-    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "2b99507a432f4e75",
-                           "bytes": 2173548058},
+                           "bytes": 1592819541},
+    "decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d34ee62a58bc973d",
+                      "bytes": 4289380021},
+    "multi_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d34ee62a58bc973d",
+                            "bytes": 4312982825},
+    "prerotated_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d34ee62a58bc973d",
+                                 "bytes": 5355693905},
+    "int8_decode_splitk": {"sources": ("decode.hip", "common.h", "kernels.h"), "digest": "d34ee62a58bc973d",
+                           "bytes": 2173660475},
 }
 
 

@@ -108,3 +108,59 @@ def test_prefill_on_both_softmax_paths(kind, shape, S, q_rows, k_row):
     print(f"[parity] {kind}: largest error at (b, row, head, dim) {tuple(int(i) for i in worst)}: "
           f"got {float(to64(out)[worst]):.5f}, want {ref[worst]:.5f}", flush=True)
     assert_close(out, ref, torch.bfloat16, f"{kind} prefill, shaped gains")
+
+
+def test_chunk_bound_counts_the_cached_prefix_keys():
+    """A later chunk's bound takes the key lengths of the cached prefix rows it
+    reads, not only its own.  One prefix key (position 150) puts all its
+    length in dims 200-201 (unrotated at p = 0.25) and was cached with a key
+    gain of 6 there, so its normalised length is ~136 against ~23 for every
+    other key.  Four chunk queries put all their length in the same two dims
+    (ordinary query gains, length ~1.45 after the scale): their score with
+    that key is ~197 (log2 units), and 2^197 overflows fp32, so those rows come
+    out finite only if the bound counts the cached key (with the chunk's own
+    keys it is ~33, under the 40 of the fixed path).  Every other query and
+    key holds zeros in dims 200-201, so no other score changes.  Global layer
+    with a separate V cache; the oracle is the multi-token decode over the
+    expected cache (prefix rows with the prefix's gains, chunk rows with the
+    chunk's)."""
+    shape = W.E_GLOBAL_LAYER
+    B, S, start, src = 1, 500, 300, 150
+    dev = device()
+    x = W.PrefillWorkload("bound_chunk", shape, B, S, torch.bfloat16, False, seed=41).draw("cpu")
+    g_big = x["g_k"].clone()
+    g_big[200:202] = 6.0
+    q, k = x["q"].clone(), x["k"].clone()
+    q[..., 200:202] = 0.0
+    k[..., 200:202] = 0.0
+    k[0, src, :, :] = 0.0
+    k[0, src, :, 200:202] = 1.0
+    aligned = [start + 7, start + 40, start + 150, start + 199]
+    for row in aligned:
+        q[0, row, :, :] = 0.0
+        q[0, row, :, 200:202] = 1.0
+    lay = api.Layer.from_shape(shape, torch.bfloat16)
+    kc = torch.zeros((B, shape.n_kv_heads, S, shape.head_dim), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    qd, kd, vd = q.to(dev), k.to(dev), x["v"].to(dev)
+    gq, gk, gbd = x["g_q"].to(dev), x["g_k"].to(dev), g_big.to(dev)
+    api.gemma_attn_prefill_chunk(lay, 0, qd[:, :start], kd[:, :start], gq, gbd, kc, v=vd[:, :start], v_cache=vc)
+    out = api.gemma_attn_prefill_chunk(lay, start, qd[:, start:], kd[:, start:], gq, gk, kc, v=vd[:, start:],
+                                       v_cache=vc)
+    torch.cuda.synchronize()
+
+    ol = oracle_layer(shape)
+    k64, v64 = to64(k), to64(x["v"])
+    kc_pre, _ = O.expected_caches_after_prefill(ol, k64[:, :start], v64[:, :start], to64(g_big), S)
+    kc_ref, vc_ref = O.expected_caches_after_prefill(ol, k64, v64, to64(x["g_k"]), S)
+    kc_ref[:, :, :start] = kc_pre[:, :, :start]
+    ref = O.decode_multi_from_cache(ol, to64(q[:, start:]), to64(x["g_q"]), kc_ref, vc_ref, np.array([S]))
+    scale = shape.head_dim ** -0.5 * LOG2E
+    qn = _normed_lengths(to64(q[0, start:]), to64(x["g_q"]), shape.norm_eps) * scale
+    kn_pre = _normed_lengths(k64[0, :start], to64(g_big), shape.norm_eps)
+    kn_own = _normed_lengths(k64[0, start:], to64(x["g_k"]), shape.norm_eps)
+    print(f"[bound] chunk: with the cached key {qn.max() * kn_pre.max():.1f}, "
+          f"with the chunk's own keys {qn.max() * kn_own.max():.1f}", flush=True)
+    assert qn.max() * kn_own.max() < 0.9 * BOUND and qn.max() * kn_pre.max() > 128
+    assert torch.isfinite(out).all(), "non-finite outputs: a bound without the cached rows"
+    assert_close(out, ref, torch.bfloat16, "global separate-V chunk against a long cached key")
