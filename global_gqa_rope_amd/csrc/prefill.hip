@@ -11,9 +11,11 @@
 //   S^T[key][row] = K~ Q~^T      32x32x16 bf16 MFMAs, A = key rows read from
 //                                LDS, B = the wave's normalised, rotated queries
 //                                held in registers
-//   online softmax per row        in registers, exp2 domain (a lane holds 16
+//   softmax per row               in registers, exp2 domain (a lane holds 16
 //                                of the 32 keys of its row, the lane 32 apart
-//                                the rest)
+//                                the rest): P = 2^S directly where QKNorm
+//                                bounds the wave's scores (score_bound_ok),
+//                                else with a running max
 //   O^T[d][row] += V^T P^T       32x32x16 MFMAs; V^T by transposing LDS reads of
 //                                the value rows, P straight from the score
 //                                registers
