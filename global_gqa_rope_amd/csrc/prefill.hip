@@ -995,8 +995,6 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
       const int masked_end = phase == 0 ? m1 : last;
       for (; kt < masked_end; ++kt) step(kt, std::true_type{}, s, s);
       if (phase == 0) {
-        // unmasked tiles two at a time, the scores alternating between two
-        // register sets (no copy of the scores per step)
         for (; kt < m2; ++kt) step(kt, std::false_type{}, s, s);
       }
     }
