@@ -597,8 +597,8 @@ __device__ __forceinline__ void tile_step(const lds_char* __restrict__ cur, lds_
 // i + 1 instead of stalling the matrix unit.  The copy of tile next_tile into
 // `nxt` spreads over those MFMAs.  NEXT = false: the last tile, no QK^T and no
 // copy.  All three stages are distinct (restrict, as for tile_step).  s_in
-// and s_out may be one array (the scores are copied first); distinct arrays
-// in alternate steps save that copy.
+// (tile i's scores) and s_out (tile i + 1's) may be one array: the scores are
+// copied first.
 // FIXED: the wave's scores are known to lie within +-kScoreBound (see
 // score_bound_ok), so P = 2^S needs no running max: no row max, no rescale
 // test and no subtraction.
